@@ -88,7 +88,9 @@ static double rd_f16(const uint8_t* p)
  * token and chunk ([r28] sec. 3.2 smem map; [r14] sec. 3.2(d) decodes the low half as
  * the fp16 scale and the high half as the signed sum). The pages do not show the
  * quantiser itself; the rounding rule is the plain reading recorded with the tests.
- * d == 0 (an all-zero block) gives q = 0 and ssum = 0.
+ * d == 0 (an all-zero block) gives q = 0 and ssum = 0. When 1/d overflows (a block
+ * of tiny values, d < 2^-128) the product x*(1/d) is infinite: it saturates to +-127,
+ * and x = 0 gives q = 0 (reading: the saturating limit of the same formula).
  */
 int qo_quantize_q8_1(const float* x, int64_t M, int64_t K,
                      int8_t* q, uint16_t* dh, int16_t* ssum)
@@ -109,9 +111,15 @@ int qo_quantize_q8_1(const float* x, int64_t M, int64_t K,
             int sum = 0;
             for (int l = 0; l < QO_QK8; ++l) {
                 volatile float v = xb[l] * id;       /* single-precision product */
-                int qi = (int)roundf(v);             /* half away from zero */
-                if (qi > 127) qi = 127;
-                if (qi < -127) qi = -127;
+                int qi;
+                if (v != v)                          /* 0 * inf: x = 0 in a block whose 1/d overflowed */
+                    qi = 0;
+                else if (v >= 127.0f)                /* saturate (covers +inf) */
+                    qi = 127;
+                else if (v <= -127.0f)
+                    qi = -127;
+                else
+                    qi = (int)roundf(v);             /* half away from zero */
                 q[i * K + c * QO_QK8 + l] = (int8_t)qi;
                 sum += qi;
             }

@@ -313,3 +313,16 @@ def test_oracle_detects_planted_mistakes():
         dsv[j] = d * sc
     no_min = np.einsum("ic,jc,ijc->ij", da, dsv, s_int)
     assert np.max(np.abs(no_min - yb)) > 0.1 * s
+
+
+def test_q8_1_overflowing_inverse_scale():
+    """A block of f32 subnormals: d = amax/127 < 2^-128, so 1/d = inf; x*(1/d) saturates to
+    +-127 and x = 0 stays 0; fp16(d) = 0 so the block contributes nothing downstream."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, :16] = np.float32(3e-40) * np.arange(1, 17, dtype=np.float32)
+    x[0, 16:31] = -np.float32(2e-40) * np.arange(1, 16, dtype=np.float32)
+    q, dh, ss = O.quantize_q8_1(x)
+    assert q[0, :16].tolist() == [127] * 16
+    assert q[0, 16:31].tolist() == [-127] * 15
+    assert q[0, 31] == 0
+    assert dh[0, 0] == 0 and ss[0, 0] == 127 * 16 - 127 * 15
