@@ -1,0 +1,124 @@
+/*
+ * qpg.h -- C ABI of libqpg.so: k-quant mixed-precision matrix multiply (MMQ) for LLM
+ * prefill on AMD Instinct MI355X (gfx950).
+ *
+ *   Y[M][N] (f32) = W[N][K] (q4_K or q6_K blocks) x q8_1(X[M][K] f32)^T
+ *
+ * The computation is the one of the minfer optimisation log ("r28 - Direction-A
+ * raw-nibble NB kernel", sec. 2.3): activations are quantised per 32 values to int8
+ * with an fp16 scale and an int16 block sum; each 32-wide (q4_K) or 16-wide (q6_K)
+ * sub-block product is an exact integer dot product; the integer sums are folded into
+ * f32 with the weight's per-sub-block scale (d*sc) and, for q4_K, the min term
+ * (-dmin*m) times the activation block sum.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers of the current HIP device. The caller owns every
+ *     buffer; the library allocates and frees nothing, prints nothing and keeps no
+ *     state besides a per-device cache of device properties.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream); nothing
+ *     synchronises. Buffers must stay valid until the stream reaches the work.
+ *   - Shapes: M = tokens, N = output features (weight rows), K = input features.
+ *     1 <= M, N; 256 <= K; K % 256 == 0; M, N, K < 2^31.
+ *   - Return value: QPG_OK (0) on success, a negative QPG_E* code otherwise. On any
+ *     error nothing has been enqueued. There is no fallback path.
+ *   - The library runs on gfx950 only (QPG_EDEVICE otherwise).
+ *
+ * Data layouts
+ *   q4_K weights: row-major, row j = K/256 consecutive 144-byte super-blocks:
+ *       +0 fp16 d, +2 fp16 dmin, +4 12 bytes of packed 6-bit (scale, min) pairs for the
+ *       eight 32-weight sub-blocks, +16 128 bytes qs (4-bit quants; byte 32p + l holds
+ *       element l of sub-block 2p in its low nibble and of sub-block 2p+1 in its high
+ *       nibble). Weight = d*sc_s*nib - dmin*m_s. (GGUF q4_K; the 144-byte stride and the
+ *       qs placement are the ones of "r28", sec. 3.2, and "r29 - NB kd-loop unroll",
+ *       sec. 3.2.) Pointer must be 16-byte aligned.
+ *   q6_K weights: row-major, row j = K/256 consecutive 210-byte super-blocks:
+ *       +0 ql[128] low 4 bits, +128 qh[64] high 2 bits, +192 int8 scales[16] (one per
+ *       16 weights), +208 fp16 d. Weight = d*sc[e/16]*(q6 - 32). (GGUF q6_K.) Pointer
+ *       must be 2-byte aligned (row starts are only 2-byte aligned when K/256 is odd).
+ *   q8_1 activations ("xq"), one buffer of qpg_q8_1_bytes(M, K) bytes, two planes:
+ *       bytes [0, M*K):            int8 q[M][K], row-major
+ *       bytes [M*K, M*K + 4*M*K/32): uint32 header[M][K/32]; low 16 bits = fp16 scale
+ *                                  d of the 32-value block, high 16 bits = int16 sum
+ *                                  of its 32 q values (the pages' "d | ssum" word).
+ *       Pointer must be 16-byte aligned.
+ *   X (f32 [M][K] row-major, 16-byte aligned) and Y (f32 [M][N] row-major, 4-byte
+ *   aligned; overwritten, never accumulated into).
+ */
+#ifndef QPG_H
+#define QPG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* qpg_stream_t;   /* hipStream_t */
+
+enum {
+    QPG_OK = 0,
+    QPG_EINVAL = -1,   /* null pointer, bad shape (M/N < 1, K % 256, too large)   */
+    QPG_EALIGN = -2,   /* a pointer violates its alignment requirement           */
+    QPG_EHIP = -3,     /* the HIP runtime reported an error when enqueuing        */
+    QPG_EDEVICE = -4   /* current device is not gfx950 or cannot be queried       */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* qpg_strerror(int status);
+
+/* Size in bytes of the q8_1 buffer for an M x K activation: M*K + 4*M*(K/32).
+ * Returns 0 when M < 1, K < 32 or K % 32 != 0. */
+size_t qpg_q8_1_bytes(int64_t M, int64_t K);
+
+/*
+ * quantize_q8_1: X f32 [M][K] -> xq (q8_1 layout above).
+ * Per 32-value block: amax = max|x|; d = amax / 127 (IEEE f32 division);
+ * q = round(x * (1/d)) with 1/d an IEEE f32 division and ties rounded away from zero
+ * (q = 0 when d = 0); sum = sum of the 32 q; stored scale = fp16(d), round to nearest
+ * even. The q values use the unrounded f32 d. Non-finite inputs are outside the
+ * contract. (q8_1 header: "r28", sec. 3.2 smem map; the rounding rule is a reading.)
+ * Here K needs only K % 32 == 0.
+ */
+int quantize_q8_1(const float* x, void* xq, int64_t M, int64_t K, qpg_stream_t stream);
+
+/*
+ * mmq_q4K / mmq_q6K: Y = W x q8_1(X)^T from f32 activations. Enqueues quantize_q8_1
+ * into the caller's workspace xq_ws (qpg_q8_1_bytes(M, K) bytes, 16-byte aligned),
+ * then the MMQ kernel (same as the _q8 entry points). On return of the stream, xq_ws
+ * holds q8_1(X).
+ * q4_K: Y[i][j] = sum_c da_ic*(d*sc)_jc*I_ijc + da_ic*ssum_ic*(-dmin*m)_jc, with
+ *       I_ijc = sum of nib*q over the 32 k of chunk c (exact int32)   ("r28", sec. 2.3)
+ * q6_K: Y[i][j] = sum_u da_{i,u/2}*(d*sc)_ju*J_iju, J = 16-wide int32 sums
+ *       ("r40 - third resident block", sec. 5: two 16-k products per 32-k chunk)
+ * The f32 summation order is the kernel's own; results agree with the exact value to
+ * |err| <= 1e-4*|y| + 1e-3*rms(Y).
+ */
+int mmq_q4K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
+            void* xq_ws, qpg_stream_t stream);
+int mmq_q6K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
+            void* xq_ws, qpg_stream_t stream);
+
+/* The MMQ kernels alone, on an already quantised q8_1 buffer xq. */
+int mmq_q4K_q8(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+               qpg_stream_t stream);
+int mmq_q6K_q8(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+               qpg_stream_t stream);
+
+/*
+ * Integer stage only: the same staging, unpack and int8 MFMA code as the _q8 entry
+ * points, writing the exact int32 sub-block sums instead of folding them.
+ *   mmq_q4K_isums: s int32 [M][N][K/32], s[i][j][c] = I_ijc
+ *   mmq_q6K_isums: s int32 [M][N][K/16], s[i][j][u] = J_iju
+ * s must be 4-byte aligned; M*N*(K/16) must be < 2^40 elements.
+ */
+int mmq_q4K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                  qpg_stream_t stream);
+int mmq_q6K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                  qpg_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QPG_H */

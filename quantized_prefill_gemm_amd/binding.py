@@ -1,0 +1,164 @@
+"""ctypes binding of libqpg.so: argument marshalling only.
+
+Every step of the path runs in the HIP kernels of libqpg.so. torch provides device
+memory and the stream (torch.cuda.current_stream()); nothing here computes. If the
+library has not been built, the first call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqpg.so")
+
+QPG_OK, QPG_EINVAL, QPG_EALIGN, QPG_EHIP, QPG_EDEVICE = 0, -1, -2, -3, -4
+
+
+class QPGError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqpg.so once. Raises if it is missing (build with __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QPGError(QPG_EINVAL, f"libqpg.so not built at {LIB_PATH}")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        L.qpg_strerror.argtypes = [ctypes.c_int]
+        L.qpg_strerror.restype = ctypes.c_char_p
+        L.qpg_q8_1_bytes.argtypes = [I64, I64]
+        L.qpg_q8_1_bytes.restype = ctypes.c_size_t
+        L.quantize_q8_1.argtypes = [P, P, I64, I64, P]
+        for f in (L.mmq_q4K, L.mmq_q6K):
+            f.argtypes = [P, P, P, I64, I64, I64, P, P]
+        for f in (L.mmq_q4K_q8, L.mmq_q6K_q8, L.mmq_q4K_isums, L.mmq_q6K_isums):
+            f.argtypes = [P, P, P, I64, I64, I64, P]
+        for f in (L.quantize_q8_1, L.mmq_q4K, L.mmq_q6K, L.mmq_q4K_q8, L.mmq_q6K_q8, L.mmq_q4K_isums,
+                  L.mmq_q6K_isums):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+EXPORTS = ("qpg_strerror", "qpg_q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8",
+           "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums")
+
+
+def _check(rc: int, what: str):
+    if rc != QPG_OK:
+        raise QPGError(rc, f"{what}: {lib().qpg_strerror(rc).decode()}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda:
+        raise QPGError(QPG_EINVAL, f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise QPGError(QPG_EINVAL, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise QPGError(QPG_EINVAL, f"{name} must be contiguous")
+
+
+def q8_1_bytes(M: int, K: int) -> int:
+    return int(lib().qpg_q8_1_bytes(M, K))
+
+
+def quantize_q8_1(x: torch.Tensor, xq: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """x f32 [M, K] (device) -> uint8 q8_1 buffer of q8_1_bytes(M, K) bytes."""
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    nbytes = q8_1_bytes(M, K)
+    if xq is None:
+        xq = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    _dev(xq, torch.uint8, "xq")
+    if xq.numel() < nbytes:
+        raise QPGError(QPG_EINVAL, "xq too small")
+    _check(lib().quantize_q8_1(_ptr(x), _ptr(xq), M, K, _stream(stream)), "quantize_q8_1")
+    return xq
+
+
+def _wcheck(w: torch.Tensor, N: int, K: int, bytes_per_block: int):
+    _dev(w, torch.uint8, "w")
+    if w.numel() != N * (K // 256) * bytes_per_block:
+        raise QPGError(QPG_EINVAL, "w size does not match N x K")
+
+
+def _mmq(which: str, w, x, N, y, xq_ws, stream):
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    _wcheck(w, N, K, 144 if which == "q4K" else 210)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, "y")
+    if xq_ws is None:
+        xq_ws = torch.empty(max(q8_1_bytes(M, K), 1), dtype=torch.uint8, device=x.device)
+    _dev(xq_ws, torch.uint8, "xq_ws")
+    if xq_ws.numel() < q8_1_bytes(M, K):
+        raise QPGError(QPG_EINVAL, "xq_ws too small")
+    fn = lib().mmq_q4K if which == "q4K" else lib().mmq_q6K
+    _check(fn(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(xq_ws), _stream(stream)), "mmq_" + which)
+    return y
+
+
+def mmq_q4K(w: torch.Tensor, x: torch.Tensor, N: int, y=None, xq_ws=None, stream=None) -> torch.Tensor:
+    """Y f32 [M, N] = q4_K W [N, K] x q8_1(x)^T; w is the raw uint8 block buffer."""
+    return _mmq("q4K", w, x, N, y, xq_ws, stream)
+
+
+def mmq_q6K(w: torch.Tensor, x: torch.Tensor, N: int, y=None, xq_ws=None, stream=None) -> torch.Tensor:
+    return _mmq("q6K", w, x, N, y, xq_ws, stream)
+
+
+def _mmq_q8(which: str, w, xq, M, N, K, out, stream, isums: bool):
+    _dev(xq, torch.uint8, "xq")
+    if xq.numel() < q8_1_bytes(M, K):
+        raise QPGError(QPG_EINVAL, "xq too small")
+    _wcheck(w, N, K, 144 if which == "q4K" else 210)
+    if isums:
+        per = 32 if which == "q4K" else 16
+        if out is None:
+            out = torch.empty((M, N, K // per), dtype=torch.int32, device=xq.device)
+        _dev(out, torch.int32, "s")
+        fn = lib().mmq_q4K_isums if which == "q4K" else lib().mmq_q6K_isums
+    else:
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+        _dev(out, torch.float32, "y")
+        fn = lib().mmq_q4K_q8 if which == "q4K" else lib().mmq_q6K_q8
+    _check(fn(_ptr(w), _ptr(xq), _ptr(out), M, N, K, _stream(stream)),
+           ("mmq_%s_isums" if isums else "mmq_%s_q8") % which)
+    return out
+
+
+def mmq_q4K_q8(w, xq, M, N, K, y=None, stream=None):
+    return _mmq_q8("q4K", w, xq, M, N, K, y, stream, False)
+
+
+def mmq_q6K_q8(w, xq, M, N, K, y=None, stream=None):
+    return _mmq_q8("q6K", w, xq, M, N, K, y, stream, False)
+
+
+def mmq_q4K_isums(w, xq, M, N, K, s=None, stream=None):
+    return _mmq_q8("q4K", w, xq, M, N, K, s, stream, True)
+
+
+def mmq_q6K_isums(w, xq, M, N, K, s=None, stream=None):
+    return _mmq_q8("q6K", w, xq, M, N, K, s, stream, True)

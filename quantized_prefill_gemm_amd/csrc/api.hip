@@ -1,0 +1,157 @@
+// C ABI of libqpg.so (declared in include/qpg.h): argument validation, device check,
+// then the kernel launches. Nothing here allocates, frees, prints or synchronises.
+#include <mutex>
+
+#include "../../include/qpg.h"
+#include "qpg_common.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // M, N, K < 2^31
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, -1 no.
+int g_dev_ok[64];
+std::mutex g_dev_mu;
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QPG_EDEVICE;
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (g_dev_ok[dev] == 0) {
+            hipDeviceProp_t p;
+            if (hipGetDeviceProperties(&p, dev) != hipSuccess) return QPG_EDEVICE;
+            const char* a = p.gcnArchName;
+            g_dev_ok[dev] = (a[0] == 'g' && a[1] == 'f' && a[2] == 'x' && a[3] == '9' && a[4] == '5' &&
+                             a[5] == '0' && (a[6] == 0 || a[6] == ':'))
+                                ? 1
+                                : -1;
+        }
+        return g_dev_ok[dev] == 1 ? QPG_OK : QPG_EDEVICE;
+    }
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_mmq_shape(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return QPG_EINVAL;
+    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return QPG_EINVAL;
+    // tile counts must fit one grid dimension
+    const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
+    if (tiles >= kMaxDim) return QPG_EINVAL;
+    return QPG_OK;
+}
+
+int status_of(hipError_t e)
+{
+    if (e == hipSuccess) return QPG_OK;
+    return QPG_EHIP;
+}
+
+int quantize_checked(const float* x, void* xq, int64_t M, int64_t K, hipStream_t s)
+{
+    if (!x || !xq) return QPG_EINVAL;
+    if (M < 1 || K < 32 || K % 32 != 0 || M >= kMaxDim || K >= kMaxDim) return QPG_EINVAL;
+    if ((M * (K / 32) * 8 + 255) / 256 >= kMaxDim) return QPG_EINVAL;
+    if (!aligned(x, 16) || !aligned(xq, 16)) return QPG_EALIGN;
+    const int dv = check_device();
+    if (dv != QPG_OK) return dv;
+    return status_of(qpg_launch_quantize_q8_1(x, xq, M, K, s));
+}
+
+int mmq_checked(bool q6, const void* w, const void* xq, float* y, int32_t* s, int64_t M, int64_t N, int64_t K,
+                hipStream_t st)
+{
+    if (!w || !xq || (!y && !s)) return QPG_EINVAL;
+    int rc = check_mmq_shape(M, N, K);
+    if (rc != QPG_OK) return rc;
+    if (s && M * N * (K / 16) >= ((int64_t)1 << 40)) return QPG_EINVAL;
+    if (!aligned(w, q6 ? 4 : 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4)))
+        return QPG_EALIGN;
+    rc = check_device();
+    if (rc != QPG_OK) return rc;
+    return status_of(q6 ? qpg_launch_mmq_q6K(w, xq, y, s, M, N, K, st)
+                        : qpg_launch_mmq_q4K(w, xq, y, s, M, N, K, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qpg_strerror(int status)
+{
+    switch (status) {
+    case QPG_OK: return "ok";
+    case QPG_EINVAL: return "invalid argument (null pointer or unsupported shape)";
+    case QPG_EALIGN: return "pointer alignment requirement violated";
+    case QPG_EHIP: return "HIP runtime error while enqueuing";
+    case QPG_EDEVICE: return "current device is not gfx950 (MI355X) or cannot be queried";
+    default: return "unknown status";
+    }
+}
+
+size_t qpg_q8_1_bytes(int64_t M, int64_t K)
+{
+    if (M < 1 || K < 32 || K % 32 != 0 || M >= kMaxDim || K >= kMaxDim) return 0;
+    return (size_t)(M * K + 4 * M * (K / 32));
+}
+
+int quantize_q8_1(const float* x, void* xq, int64_t M, int64_t K, qpg_stream_t stream)
+{
+    return quantize_checked(x, xq, M, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q4K_q8(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!y) return QPG_EINVAL;
+    return mmq_checked(false, w, xq, y, nullptr, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_q8(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!y) return QPG_EINVAL;
+    return mmq_checked(true, w, xq, y, nullptr, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q4K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                  qpg_stream_t stream)
+{
+    if (!s) return QPG_EINVAL;
+    return mmq_checked(false, w, xq, nullptr, s, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                  qpg_stream_t stream)
+{
+    if (!s) return QPG_EINVAL;
+    return mmq_checked(true, w, xq, nullptr, s, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+static int mmq_f32(bool q6, const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K, void* xq_ws,
+                   qpg_stream_t stream)
+{
+    if (!w || !x || !y || !xq_ws) return QPG_EINVAL;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int rc = check_mmq_shape(M, N, K);
+    if (rc != QPG_OK) return rc;
+    if (!aligned(x, 16) || !aligned(xq_ws, 16) || !aligned(w, q6 ? 4 : 16) || !aligned(y, 4)) return QPG_EALIGN;
+    rc = quantize_checked(x, xq_ws, M, K, s);
+    if (rc != QPG_OK) return rc;
+    return mmq_checked(q6, w, xq_ws, y, nullptr, M, N, K, s);
+}
+
+int mmq_q4K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K, void* xq_ws,
+            qpg_stream_t stream)
+{
+    return mmq_f32(false, w, x, y, M, N, K, xq_ws, stream);
+}
+
+int mmq_q6K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K, void* xq_ws,
+            qpg_stream_t stream)
+{
+    return mmq_f32(true, w, x, y, M, N, K, xq_ws, stream);
+}
+
+}  // extern "C"

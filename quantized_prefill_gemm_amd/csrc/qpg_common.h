@@ -1,0 +1,57 @@
+// Internal definitions shared by the gfx950 kernels of libqpg (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qpg {
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef int int32x16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int QK_K = 256;        // weights per super-block
+constexpr int QK8 = 32;          // values per q8_1 block (one "chunk" of K)
+constexpr int Q4K_BYTES = 144;
+constexpr int Q6K_BYTES = 210;
+
+// Bits of the f32 value 1.5 * 2^23. An integer |v| < 2^22 added to these bits gives the
+// bits of the f32 value 1.5*2^23 + v exactly (all such values share one exponent and
+// unit spacing), so an int32 MFMA accumulating onto this constant delivers its integer
+// sum already "converted": F = 1.5*2^23 + I, with no v_cvt instruction.
+constexpr int MAGIC_BITS = 0x4B400000;
+constexpr float MAGIC_F = 12582912.0f;
+
+// C/D layout of the 32x32 MFMAs (verified by a lane probe on gfx950): lane l, register
+// r holds row 8*(r>>2) + 4*(l>>5) + (r&3), column l&31. A and B operands: lane l holds
+// row (A) / column (B) l&31 and the K-group l>>5 (16 bytes of int8, or 8 bf16).
+__device__ __forceinline__ int c_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t h)
+{
+    _Float16 v;
+    uint16_t b = (uint16_t)h;
+    __builtin_memcpy(&v, &b, 2);
+    return (float)v;
+}
+
+// Round-to-nearest-even f32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (u + 0x7FFFu + lsb) >> 16;
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+}  // namespace qpg
+
+// Kernel launchers (defined in the .hip files; called by the C ABI layer after the
+// arguments have been validated). They return hipGetLastError() of the launch.
+hipError_t qpg_launch_quantize_q8_1(const float* x, void* xq, int64_t M, int64_t K, hipStream_t s);
+hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* isums,
+                              int64_t M, int64_t N, int64_t K, hipStream_t s);
+hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums,
+                              int64_t M, int64_t N, int64_t K, hipStream_t s);

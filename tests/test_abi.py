@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI (no kernel is ever launched here).
+
+The library must load, export every function include/qpg.h declares, and reject bad
+arguments with the documented status before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qpg.h")
+LIB = os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg.so")
+
+EINVAL, EALIGN, EDEVICE = -1, -2, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_0-9A-Z]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.skip("libqpg.so not built")
+    lib = ctypes.CDLL(LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.qpg_strerror.restype = ctypes.c_char_p
+    lib.qpg_q8_1_bytes.restype = ctypes.c_size_t
+    lib.qpg_q8_1_bytes.argtypes = [I64, I64]
+    lib.quantize_q8_1.argtypes = [P, P, I64, I64, P]
+    for f in (lib.mmq_q4K, lib.mmq_q6K):
+        f.argtypes = [P, P, P, I64, I64, I64, P, P]
+    for f in (lib.mmq_q4K_q8, lib.mmq_q6K_q8, lib.mmq_q4K_isums, lib.mmq_q6K_isums):
+        f.argtypes = [P, P, P, I64, I64, I64, P]
+    return lib
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8", "mmq_q6K_q8", "mmq_q4K_isums",
+              "mmq_q6K_isums", "qpg_q8_1_bytes", "qpg_strerror"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_binding_names_match_header():
+    from quantized_prefill_gemm_amd import binding
+    assert set(declared_functions()) == set(binding.EXPORTS)
+
+
+def test_strerror_and_sizes(L):
+    for code in (0, -1, -2, -3, -4, -99):
+        assert L.qpg_strerror(code)
+    assert L.qpg_q8_1_bytes(512, 4096) == 512 * 4096 + 4 * 512 * 128
+    assert L.qpg_q8_1_bytes(1, 32) == 36
+    assert L.qpg_q8_1_bytes(0, 256) == 0
+    assert L.qpg_q8_1_bytes(4, 48) == 0
+
+
+A16 = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: every call below fails validation
+A2 = ctypes.c_void_p((1 << 20) + 2)
+A8 = ctypes.c_void_p((1 << 20) + 8)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, A16, 4, 256), EINVAL),
+    ((A16, None, 4, 256), EINVAL),
+    ((A16, A16, 0, 256), EINVAL),
+    ((A16, A16, 4, 0), EINVAL),
+    ((A16, A16, 4, 48), EINVAL),
+    ((A16, A16, 1 << 31, 256), EINVAL),
+    ((A8, A16, 4, 256), EALIGN),
+    ((A16, A8, 4, 256), EALIGN),
+])
+def test_quantize_rejects(L, args, expect):
+    assert L.quantize_q8_1(*args, None) == expect
+
+
+@pytest.mark.parametrize("fn", ["mmq_q4K_q8", "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums"])
+@pytest.mark.parametrize("args,expect", [
+    ((None, A16, A16, 64, 256, 256), EINVAL),
+    ((A16, None, A16, 64, 256, 256), EINVAL),
+    ((A16, A16, None, 64, 256, 256), EINVAL),
+    ((A16, A16, A16, 0, 256, 256), EINVAL),
+    ((A16, A16, A16, 64, 0, 256), EINVAL),
+    ((A16, A16, A16, 64, 256, 128), EINVAL),
+    ((A16, A16, A16, 64, 256, 288), EINVAL),
+    ((A16, A16, A16, 64, 1 << 31, 256), EINVAL),
+    ((A16, A8, A16, 64, 256, 256), EALIGN),
+])
+def test_mmq_q8_rejects(L, fn, args, expect):
+    assert getattr(L, fn)(*args, None) == expect
+
+
+def test_alignment_rules_per_type(L):
+    # q4_K weights need 16-byte alignment, q6_K weights 4-byte
+    assert L.mmq_q4K_q8(A8, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K_q8(A2, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q4K(A16, A8, A16, 64, 256, 256, A16, None) == EALIGN     # x
+    assert L.mmq_q4K(A16, A16, A16, 64, 256, 256, A8, None) == EALIGN     # workspace
+    assert L.mmq_q6K(A16, A16, A16, 64, 256, 256, None, None) == EINVAL   # missing workspace
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_has_gpu(), reason="device check path is only exercised where no GPU exists")
+def test_valid_call_without_device_reports_edevice(L):
+    # All arguments valid: validation passes and the device query fails -> QPG_EDEVICE,
+    # nothing is enqueued.
+    assert L.mmq_q4K_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
+    assert L.quantize_q8_1(A16, A16, 64, 256, None) == EDEVICE

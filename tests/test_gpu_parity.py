@@ -1,0 +1,207 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (from the method's stated targets):
+  * q8_1 output (int8 values, fp16 scale bits, int16 block sums): bit-exact.
+  * integer sub-block sums (isums entry points): bit-exact.
+  * f32 outputs: |gpu - oracle| <= 1e-4*|oracle| + 1e-3*rms(oracle) element-wise, the
+    oracle being exact up to fp64 summation.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from oracle import oracle as O
+from qblocks import tolerance_ok, encode_q4K
+from quantized_prefill_gemm_amd import binding as B
+from quantized_prefill_gemm_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def parse_q8(buf: torch.Tensor, M: int, K: int):
+    b = buf.cpu().numpy()
+    q = b[:M * K].view(np.int8).reshape(M, K)
+    hdr = b[M * K:M * K + 4 * M * (K // 32)].view(np.uint32).reshape(M, K // 32)
+    dh = (hdr & 0xFFFF).astype(np.uint16)
+    ss = (hdr >> 16).astype(np.uint16).view(np.int16)
+    return q, dh, ss
+
+
+def gpu_quantize(x: np.ndarray):
+    M, K = x.shape
+    xq = B.quantize_q8_1(dev(x))
+    torch.cuda.synchronize()
+    return xq, parse_q8(xq, M, K)
+
+
+def assert_q8_equal(x: np.ndarray, tag: str):
+    _, (q, dh, ss) = gpu_quantize(x)
+    rq, rdh, rss = O.quantize_q8_1(x)
+    assert np.array_equal(q, rq), f"{tag}: q mismatch at {np.argwhere(q != rq)[:5]}"
+    assert np.array_equal(dh, rdh), f"{tag}: fp16 scale mismatch"
+    assert np.array_equal(ss, rss), f"{tag}: block sum mismatch"
+
+
+# ----------------------------------------------------------------------------- q8_1
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_quantize_bitexact_configs(cfg):
+    say(f"[quantize cfg{cfg}]")
+    _, M, N, K, _, X = inputs.make_config(cfg)
+    assert_q8_equal(X, f"cfg{cfg}")
+
+
+def test_quantize_edge_cases():
+    say("[quantize edges]")
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "q8_1_ties.json")))
+    rng = np.random.default_rng(9)
+    cases = {
+        "zeros": np.zeros((3, 256), np.float32),
+        "ties": np.tile(np.array(g["x"], np.float32), (2, 8)),
+        "tiny": (rng.standard_normal((4, 256)) * 1e-30).astype(np.float32),
+        "subnormal_scale": (rng.standard_normal((4, 256)) * 1e-39).astype(np.float32),
+        "huge": (rng.standard_normal((4, 256)) * 3e4).astype(np.float32),
+        "outlier": np.where(rng.random((8, 512)) < 0.01, 900.0, rng.standard_normal((8, 512)) * 0.1).astype(np.float32),
+        "k32": rng.standard_normal((7, 32)).astype(np.float32),
+        "k96": rng.standard_normal((5, 96)).astype(np.float32),
+        "m1": rng.standard_normal((1, 4096)).astype(np.float32),
+        "ramp": (np.arange(64 * 256, dtype=np.float32).reshape(64, 256) % 97 - 48.5) / 7,
+    }
+    for tag, x in cases.items():
+        assert_q8_equal(x, tag)
+
+
+# ----------------------------------------------------------------------------- integer stage
+
+def gpu_isums(wtype, W, xq, M, N, K):
+    fn = B.mmq_q4K_isums if wtype == "q4_K" else B.mmq_q6K_isums
+    s = fn(dev(W.reshape(-1)), xq, M, N, K)
+    torch.cuda.synchronize()
+    return s.cpu().numpy()
+
+
+ISUM_SHAPES = [(64, 256, 256), (1, 1, 256), (33, 130, 512), (65, 257, 768), (128, 384, 1024), (7, 129, 2816)]
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("M,N,K", ISUM_SHAPES)
+def test_isums_bitexact(wtype, M, N, K):
+    say(f"[isums {wtype} {M}x{N}x{K}]")
+    W, X = inputs.small_case(wtype, M, N, K, seed=3)
+    xq, (q, _, _) = gpu_quantize(X)
+    s = gpu_isums(wtype, W, xq, M, N, K)
+    ref = O.isums(wtype, W, q)
+    assert np.array_equal(s, ref), f"mismatches: {np.count_nonzero(s != ref)}"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4])
+def test_isums_bitexact_config_rows(cfg):
+    """Integer sums of the real workloads on a slice of weight rows (all tokens, all K)."""
+    wtype, M, N, K, W, X = inputs.make_config(cfg)
+    rows = slice(0, min(N, 256))
+    Wr = np.ascontiguousarray(W[rows])
+    n = Wr.shape[0]
+    say(f"[isums cfg{cfg} rows {n}]")
+    xq, (q, _, _) = gpu_quantize(X)
+    s = gpu_isums(wtype, Wr, xq, M, n, K)
+    assert np.array_equal(s, O.isums(wtype, Wr, q))
+
+
+# ----------------------------------------------------------------------------- outputs
+
+def gpu_mmq(wtype, W, X, N):
+    fn = B.mmq_q4K if wtype == "q4_K" else B.mmq_q6K
+    y = fn(dev(W.reshape(-1)), dev(X), N)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def check_out(g, r, tag):
+    ok, ratio, relmax = tolerance_ok(g, r)
+    say(f"  {tag}: worst err/bound {ratio:.3e}, max rel err (|r|>=rms) {relmax:.3e}")
+    assert ok, f"{tag}: err/bound {ratio}"
+    assert relmax < 1e-4, f"{tag}: relative error {relmax}"
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_mmq_configs_full(cfg):
+    wtype, M, N, K, W, X = inputs.make_config(cfg)
+    say(f"[mmq cfg{cfg} {wtype} {M}x{N}x{K}]")
+    g = gpu_mmq(wtype, W, X, N)
+    r = O.mmq(wtype, W, X)
+    check_out(g, r, f"cfg{cfg}")
+
+
+TAIL_SHAPES = [(1, 1, 256), (1, 130, 512), (33, 1, 256), (33, 130, 768), (65, 257, 512), (100, 300, 1280),
+               (64, 128, 256), (63, 127, 4096)]
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+@pytest.mark.parametrize("M,N,K", TAIL_SHAPES)
+def test_mmq_tails(wtype, M, N, K):
+    say(f"[mmq tail {wtype} {M}x{N}x{K}]")
+    W, X = inputs.small_case(wtype, M, N, K, seed=5, gain=True)
+    check_out(gpu_mmq(wtype, W, X, N), O.mmq(wtype, W, X), f"{wtype} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+def test_f32_entry_equals_quantize_then_q8(wtype):
+    M, N, K = 96, 200, 1024
+    say(f"[f32 entry == q8 entry {wtype}]")
+    W, X = inputs.small_case(wtype, M, N, K, seed=6)
+    y1 = gpu_mmq(wtype, W, X, N)
+    xq = B.quantize_q8_1(dev(X))
+    fn = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
+    y2 = fn(dev(W.reshape(-1)), xq, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(y1, y2.cpu().numpy())
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+def test_metamorphic_bitexact(wtype):
+    """Y(-X) = -Y(X) and Y(2^t X) = 2^t Y(X), bit for bit on the GPU (no oracle needed)."""
+    M, N, K = 64, 256, 2048
+    say(f"[metamorphic {wtype}]")
+    W, X = inputs.small_case(wtype, M, N, K, seed=7)
+    y = gpu_mmq(wtype, W, X, N)
+    assert np.array_equal(gpu_mmq(wtype, W, -X, N), -y)
+    for t in (-4, 3):
+        assert np.array_equal(gpu_mmq(wtype, W, X * np.float32(2.0 ** t), N), y * np.float32(2.0 ** t))
+
+
+def test_closed_form_scale_path_on_gpu():
+    """All nib = 1, sc = 1, d = 1, X = 1: Y = K * 0.99993896484375 exactly (golden)."""
+    K = 1024
+    w = np.tile(encode_q4K(1.0, 0.0, [1] * 8, [0] * 8, [1] * 256), (130, K // 256))
+    y = gpu_mmq("q4_K", w, np.ones((70, K), np.float32), 130)
+    assert np.all(y == np.float32(1023.9375))
+
+
+def test_stack_sampled_rows():
+    """7B-style stack (M = 1024): each of the 4 distinct GEMM shapes of layer 0 and a later
+    layer, full GPU GEMM, 16 sampled weight rows checked against the oracle."""
+    rng = np.random.default_rng(17)
+    for layer in (0, 31):
+        for idx in (0, 2, 4, 6):           # q (q4_K 4096^2), v (q6_K 4096^2), gate, down
+            name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
+            X = inputs.make_stack_input(layer, idx)
+            say(f"[stack layer {layer} {name} {wtype} {X.shape[0]}x{N}x{K}]")
+            g = gpu_mmq(wtype, W, X, N)
+            rows = np.sort(rng.choice(N, 16, replace=False))
+            r = O.mmq(wtype, W[rows], X)
+            check_out(g[:, rows], r, f"stack L{layer} {name}")
