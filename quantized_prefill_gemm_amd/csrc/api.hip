@@ -7,7 +7,8 @@
 
 namespace {
 
-constexpr int64_t kMaxDim = (int64_t)1 << 31;   // M, N, K < 2^31
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // M, N < 2^31
+constexpr int64_t kMaxK = (int64_t)1 << 24;     // K <= 2^24 keeps every per-tile byte offset < 2^31
 
 // Per-device "is gfx950" cache: 0 unknown, 1 yes, -1 no.
 int g_dev_ok[64];
@@ -37,7 +38,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int check_mmq_shape(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return QPG_EINVAL;
-    if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return QPG_EINVAL;
+    if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return QPG_EINVAL;
     // tile counts must fit one grid dimension
     const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
     if (tiles >= kMaxDim) return QPG_EINVAL;

@@ -10,22 +10,29 @@
 //
 // MI355X design (not the pages' GB10 one):
 //  * Workgroup tile 64 tokens x 128 weight rows, 4 waves; wave w owns weight rows
-//    32w..32w+31 of the tile and all 64 tokens (two 32x32 output sub-tiles).
-//  * Per super-block (256 k) the workgroup stages, with 16-byte coalesced global loads,
-//    the raw q4_K qs bytes (128 B per row) and the q8_1 int8 tile into LDS, and decodes
-//    the block headers once into per-(row, sub-block) f32 terms.
-//  * Integer stage: one v_mfma_i32_32x32x32_i8 per (32x32 sub-tile, chunk). K = 32 is
-//    exactly one q8_1 block and one q4_K sub-block, so no two scales ever share an
-//    integer accumulator. A 16-byte LDS read of raw qs serves two chunks: the low
-//    nibbles (& 0x0F0F0F0F) are chunk 2p, the high nibbles (>> 4 & 0x0F0F0F0F) chunk 2p+1.
+//    32w..32w+31 and all 64 tokens: two 32x32 output sub-tiles with the WEIGHT rows on
+//    the MFMA row side and the tokens on the column side, so each lane's 16 accumulators
+//    share one token: da is one register per lane, the per-row d*sc is read once per
+//    chunk and serves both token sub-tiles.
+//  * Per super-block (256 k) the workgroup stages, with 16-byte buffer loads (hardware
+//    range checks give zeros past the last token / row, no branches), the raw qs bytes
+//    (128 B per row) and the q8_1 int8 tile into XOR-swizzled LDS, and decodes the block
+//    headers once into per-(row, sub-block) f32 terms.
+//  * Integer stage: one v_mfma_i32_32x32x32_i8 per (sub-tile, chunk). K = 32 is exactly
+//    one q8_1 block and one q4_K sub-block, so no two scales share an integer
+//    accumulator. One 16-byte LDS read of raw qs serves two chunks: low nibbles
+//    (& 0x0F0F0F0F) are chunk 2p, high nibbles (>> 4 & 0x0F0F0F0F) chunk 2p+1.
 //  * The MFMA accumulates onto the bits of 1.5*2^23, so its int32 result read as f32 is
-//    1.5*2^23 + I exactly (|I| <= 15*127*32 < 2^22). One FMA with the per-row constant
-//    c0 = -1.5*2^23*dsv gives round(dsv*I) (dsv has <= 17 significant bits, so c0 is
-//    exact), and a second FMA with da accumulates: two VALU ops per output per chunk.
-//  * Min term: per super-block, sum_s (da*ssum)_is * m_js is a K=8 product. da*ssum is an
-//    exact f32 (11 + 12 bits); it is split into three bf16 pieces whose sum is exact,
-//    m (0..63) is exact in bf16, and two v_mfma_f32_32x32x16_bf16 form the product with
-//    f32 accumulation; one FMA with -dmin per super-block folds it into Y.
+//    1.5*2^23 + I exactly (|I| <= 15*127*32 < 2^22). e = fma(F, da, -1.5*2^23*da) is
+//    round(da*I) (the constant is exact: da has 11 significant bits), and
+//    y = fma(e, dsv, y) accumulates: two VALU ops per output per chunk, nothing else.
+//    MFMAs are issued one step ahead of the fold that consumes them, so the matrix core
+//    runs while the VALU folds the previous result.
+//  * Min term, entirely on the matrix core: per super-block, sum_s dmv_js * (da*ssum)_is
+//    is a K=8 product. Both factors are exact f32 (17 and 23 significant bits); each is
+//    split into three bf16 pieces that sum to it exactly, and three
+//    v_mfma_f32_32x32x16_bf16 accumulate the six significant piece products
+//    (w1x1 w1x2 w2x1 w1x3 w3x1 w2x2, dropped terms < 2^-23 relative) straight into y.
 //  * The "isums" instantiation runs the same staging, unpack and MFMA code and stores the
 //    integer sums instead of folding them (the bit-exact witness of the integer stage).
 #include "qpg_common.h"
@@ -37,21 +44,16 @@ typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 64;            // tokens per workgroup tile
 constexpr int TN = 128;           // weight rows per workgroup tile
-constexpr int AQ_STRIDE = 272;    // LDS bytes per token row of the q tile (256 + 16 pad)
-constexpr int BQ_STRIDE = 144;    // LDS bytes per weight row of the qs tile (128 + 16 pad)
-constexpr int BS_STRIDE = 80;     // per weight row: dsv[8] f32, c0[8] f32, m[8] bf16
-constexpr int AX_STRIDE = 48;     // per token: x1[8], x2[8], x3[8] bf16 pieces of da*ssum
+constexpr int DA_STRIDE = 20;     // floats per token: per chunk pair p: da_2p, da_2p+1, c0_2p, c0_2p+1 (+pad)
+constexpr int PC_STRIDE = 24;     // bf16 per token / row: three pieces x 8 sub-blocks
 
-// Strides are chosen so that 16 lanes reading 16 bytes each at consecutive rows hit 16
-// distinct 16-byte bank groups of the 64-bank LDS (stride mod 256 is an odd multiple of
-// 16 or 48/80/144-type values whose multiples are distinct mod 256).
 struct alignas(16) Smem {
-    alignas(16) uint8_t aq[TM * AQ_STRIDE];          // q8_1 int8 tile of the super-block
-    alignas(16) float ada[8][2][2][16];              // da in C-register order: [chunk][subtile][k-group][r]
-    alignas(16) uint8_t ax[TM * AX_STRIDE];          // min-term A operand pieces
-    alignas(16) uint8_t bq[TN * BQ_STRIDE];          // raw qs bytes of the super-block
-    alignas(16) uint8_t bs[TN * BS_STRIDE];          // decoded per-(row, sub-block) scale terms
-    alignas(16) float bnd[TN];                       // -dmin per row
+    alignas(16) uint8_t aq[TM * 256];          // q8 tile, granule g of token t at 16*(g ^ (t & 15))
+    alignas(16) uint8_t bq[TN * 128];          // raw qs, granule g of row j at 16*(g ^ ((j >> 1) & 7))
+    alignas(16) float bdsv[8][TN];             // d*sc per chunk, rows in C-register order per wave
+    alignas(16) float ada[TM * DA_STRIDE];     // da and -1.5*2^23*da per token and chunk
+    alignas(16) uint16_t ax[TM * PC_STRIDE];   // bf16 pieces of da*ssum per token
+    alignas(16) uint16_t bw[TN * PC_STRIDE];   // bf16 pieces of -dmin*m per row
 };
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
@@ -67,13 +69,30 @@ __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_
     n_tile = t / tiles_m;
 }
 
+// Position of weight row jj (0..31 inside a wave's rows) in C-register order: k-group
+// (jj >> 2) & 1 holds registers r = 4*(jj >> 3) + (jj & 3).
+__device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
+
+__device__ __forceinline__ void split3_bf16(float v, uint16_t* dst, int stride)
+{
+    // v = b1 + b2 + b3 exactly for v with <= 24 significant bits
+    const uint32_t b1 = f32_to_bf16_bits(v);
+    const float r1 = v - bf16_bits_to_f32(b1);
+    const uint32_t b2 = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(b2);
+    const uint32_t b3 = f32_to_bf16_bits(r2);
+    dst[0] = (uint16_t)b1;
+    dst[stride] = (uint16_t)b2;
+    dst[2 * stride] = (uint16_t)b3;
+}
+
 template <bool ISUMS>
-__global__ void __launch_bounds__(256) mmq_q4K_kernel(const uint8_t* __restrict__ W,
-                                                      const int8_t* __restrict__ qplane,
-                                                      const uint32_t* __restrict__ hdr,
-                                                      float* __restrict__ Y,
-                                                      int32_t* __restrict__ S,
-                                                      int M, int N, int K, int tiles_m, int total)
+__global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
+                                                         const int8_t* __restrict__ qplane,
+                                                         const uint32_t* __restrict__ hdr,
+                                                         float* __restrict__ Y,
+                                                         int32_t* __restrict__ S,
+                                                         int M, int N, int K, int tiles_m, int total)
 {
     __shared__ Smem sm;
     int m_tile, n_tile;
@@ -82,8 +101,17 @@ __global__ void __launch_bounds__(256) mmq_q4K_kernel(const uint8_t* __restrict_
     const int hg = lane >> 5, l32 = lane & 31;
     const int m0 = m_tile * TM, n0 = n_tile * TN;
     const int nsb = K / QK_K, nc = K / QK8;
-    const size_t wrow = (size_t)nsb * Q4K_BYTES;
-    const int jl = 32 * wave + l32;      // this lane's weight row within the tile
+    const int wrow = nsb * Q4K_BYTES;
+
+    // Buffer descriptors over this tile's rows only: loads past the last token / weight
+    // row of the matrix fall outside num_records and return zeros.
+    const int rows_w = min(TN, N - n0), rows_t = min(TM, M - m0);
+    const __amdgpu_buffer_rsrc_t rW =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * wrow), 0, rows_w * wrow, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rQ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qplane + (size_t)m0 * K), 0, rows_t * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
     int32x16 magic;
 #pragma unroll
@@ -94,57 +122,49 @@ __global__ void __launch_bounds__(256) mmq_q4K_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
+    const int wr = 32 * wave + l32;                 // weight row of this lane's A operand
+    const int wsw = (wr >> 1) & 7;                   // its LDS swizzle
+    int tk[2], tsw[2];
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) {
+        tk[ts] = 32 * ts + l32;                      // token of this lane's B operand / outputs
+        tsw[ts] = tk[ts] & 15;
+    }
+
     for (int sb = 0; sb < nsb; ++sb) {
-        // ---------------- stage A: q8 tile (64 tokens x 256 B), 16-byte granules
+        // ---------------- stage A: q8 tile (64 tokens x 256 B)
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int g = it * 256 + tid, t = g >> 4, part = g & 15;
-            int32x4 v = {0, 0, 0, 0};
-            if (m0 + t < M)
-                v = *reinterpret_cast<const int32x4*>(qplane + (size_t)(m0 + t) * K + sb * QK_K + part * 16);
-            *reinterpret_cast<int32x4*>(sm.aq + t * AQ_STRIDE + part * 16) = v;
+            const int g = it * 256 + tid, t = g >> 4, gi = g & 15;
+            const int32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rQ, t * K + sb * QK_K + gi * 16, 0, 0);
+            *reinterpret_cast<int32x4*>(sm.aq + t * 256 + 16 * (gi ^ (t & 15))) = v;
         }
-        // ---------------- stage A: headers -> da (C order) and bf16 pieces of da*ssum
+        // ---------------- stage A: headers -> da, -1.5*2^23*da, bf16 pieces of da*ssum
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int h = it * 256 + tid, t = h >> 3, c = h & 7;
-            uint32_t hw = 0;
-            if (m0 + t < M) hw = hdr[(size_t)(m0 + t) * nc + sb * 8 + c];
+            const uint32_t hw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rH, (t * nc + sb * 8 + c) * 4, 0, 0);
             const float da = half_bits_to_float(hw & 0xFFFFu);
-            const float xs = da * (float)(int16_t)(hw >> 16);            // exact
-            const int a = t >> 5, tt = t & 31;
-            sm.ada[c][a][(tt >> 2) & 1][4 * (tt >> 3) + (tt & 3)] = da;
-            const uint32_t b1 = f32_to_bf16_bits(xs);
-            const float r1 = xs - bf16_bits_to_f32(b1);                    // exact
-            const uint32_t b2 = f32_to_bf16_bits(r1);
-            const float r2 = r1 - bf16_bits_to_f32(b2);                    // exact
-            const uint32_t b3 = f32_to_bf16_bits(r2);                      // r2 has <= 8 bits
-            uint16_t* ax = reinterpret_cast<uint16_t*>(sm.ax + t * AX_STRIDE);
-            ax[c] = (uint16_t)b1;
-            ax[8 + c] = (uint16_t)b2;
-            ax[16 + c] = (uint16_t)b3;
+            float* ad = sm.ada + t * DA_STRIDE + 4 * (c >> 1) + (c & 1);
+            ad[0] = da;
+            ad[2] = -MAGIC_F * da;                                  // exact
+            split3_bf16(da * (float)(int16_t)(hw >> 16), sm.ax + t * PC_STRIDE + c, 8);   // da*ssum exact
         }
         // ---------------- stage B: raw qs (128 rows x 128 B)
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int g = it * 256 + tid, j = g >> 3, part = g & 7;
-            int32x4 v = {0, 0, 0, 0};
-            if (n0 + j < N)
-                v = *reinterpret_cast<const int32x4*>(W + (size_t)(n0 + j) * wrow + (size_t)sb * Q4K_BYTES + 16 +
-                                                      part * 16);
-            *reinterpret_cast<int32x4*>(sm.bq + j * BQ_STRIDE + part * 16) = v;
+            const int g = it * 256 + tid, j = g >> 3, gi = g & 7;
+            const int32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rW, j * wrow + sb * Q4K_BYTES + 16 + gi * 16, 0, 0);
+            *reinterpret_cast<int32x4*>(sm.bq + j * 128 + 16 * (gi ^ ((j >> 1) & 7))) = v;
         }
-        // ---------------- stage B: decode d, dmin and the eight 6-bit (sc, m) pairs
+        // ---------------- stage B: d, dmin and the eight 6-bit (sc, m) pairs of each row
         if (tid < TN) {
             const int j = tid;
-            uint32x4 hv = {0u, 0u, 0u, 0u};
-            if (n0 + j < N)
-                hv = *reinterpret_cast<const uint32x4*>(W + (size_t)(n0 + j) * wrow + (size_t)sb * Q4K_BYTES);
-            const float d = half_bits_to_float(hv[0] & 0xFFFFu);
-            const float dmin = half_bits_to_float(hv[0] >> 16);
-            const uint32_t S0 = hv[1], S1 = hv[2], S2 = hv[3];   // packed bytes 0-3, 4-7, 8-11
-            float* bs = reinterpret_cast<float*>(sm.bs + j * BS_STRIDE);
-            uint16_t* bm = reinterpret_cast<uint16_t*>(sm.bs + j * BS_STRIDE + 64);
+            const int32x4 hv = __builtin_amdgcn_raw_buffer_load_b128(rW, j * wrow + sb * Q4K_BYTES, 0, 0);
+            const float d = half_bits_to_float((uint32_t)hv[0] & 0xFFFFu);
+            const float dmin = half_bits_to_float((uint32_t)hv[0] >> 16);
+            const uint32_t S0 = (uint32_t)hv[1], S1 = (uint32_t)hv[2], S2 = (uint32_t)hv[3];
+            const int pos = 32 * (j >> 5) + c_pos(j & 31);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 uint32_t sc, m;
@@ -156,94 +176,123 @@ __global__ void __launch_bounds__(256) mmq_q4K_kernel(const uint8_t* __restrict_
                     sc = ((S2 >> s4) & 15u) | (((S0 >> s4) >> 6 & 3u) << 4);
                     m = ((S2 >> s4) >> 4 & 15u) | (((S1 >> s4) >> 6 & 3u) << 4);
                 }
-                const float dsv = d * (float)sc;                           // exact (17 bits)
-                bs[s] = dsv;
-                bs[8 + s] = -MAGIC_F * dsv;                                 // exact
-                bm[s] = (uint16_t)(__float_as_uint((float)m) >> 16);       // m exact in bf16
+                sm.bdsv[s][pos] = d * (float)sc;                      // exact (17 bits)
+                split3_bf16(-(dmin * (float)m), sm.bw + j * PC_STRIDE + s, 8);   // exact (17 bits)
             }
-            sm.bnd[j] = -dmin;
         }
         __syncthreads();
 
-        // ---------------- compute: 8 chunks x 2 sub-tiles, then the min term
-        const floatx4* bsp = reinterpret_cast<const floatx4*>(sm.bs + jl * BS_STRIDE);
-        const floatx4 dsv_lo = bsp[0], dsv_hi = bsp[1], c0_lo = bsp[2], c0_hi = bsp[3];
+        // ---------------- integer stage + fold, MFMA one step ahead of the fold
+        // Step k = 0..15 is (chunk c = k/2, token sub-tile ts = k%2). In step k the wave
+        // issues the LDS reads for step k+1, the MFMA of step k+1, then folds step k; the
+        // scheduling barriers keep that order, so only two accumulator blocks and one set
+        // of operands are live at a time.
+        auto a_from = [&](const uint32x4& raw, int c) -> int32x4 {
+            const uint32x4 u = (c & 1) ? ((raw >> 4u) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
+            int32x4 r;
+            __builtin_memcpy(&r, &u, 16);
+            return r;
+        };
+        auto ld_raw = [&](int p) -> uint32x4 {
+            return *reinterpret_cast<const uint32x4*>(sm.bq + wr * 128 + 16 * ((2 * p + hg) ^ wsw));
+        };
+        auto ld_b = [&](int c, int ts) -> int32x4 {
+            return *reinterpret_cast<const int32x4*>(sm.aq + tk[ts] * 256 + 16 * ((2 * c + hg) ^ tsw[ts]));
+        };
+
+        uint32x4 raw = ld_raw(0);
+        int32x16 F[2];
+        F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, 0), ld_b(0, 0), magic, 0, 0, 0);
+        floatx4 dsv[4];
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32x4 raw = *reinterpret_cast<const uint32x4*>(sm.bq + jl * BQ_STRIDE + 32 * p + 16 * hg);
+        for (int k = 0; k < 16; ++k) {
+            const int c = k >> 1, ts = k & 1;
+            const int k1 = k + 1, c1 = k1 >> 1, ts1 = k1 & 1;
+            int32x4 bn;
+            if (k1 < 16) {
+                if ((k1 & 3) == 0) raw = ld_raw(k1 >> 2);
+                bn = ld_b(c1, ts1);
+            }
+            if constexpr (!ISUMS) {
+                if (ts == 0) {
+                    const floatx4* dsvp = reinterpret_cast<const floatx4*>(&sm.bdsv[c][32 * wave + 16 * hg]);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int c = 2 * p + half;
-                const uint32x4 bu = half ? ((raw >> 4u) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
-                int32x4 b;
-                __builtin_memcpy(&b, &bu, 16);
-                const float dsv = c < 4 ? dsv_lo[c & 3] : dsv_hi[c & 3];
-                const float c0 = c < 4 ? c0_lo[c & 3] : c0_hi[c & 3];
-#pragma unroll
-                for (int a = 0; a < 2; ++a) {
-                    const int32x4 av =
-                        *reinterpret_cast<const int32x4*>(sm.aq + (32 * a + l32) * AQ_STRIDE + 32 * c + 16 * hg);
-                    const int32x16 F = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, magic, 0, 0, 0);
-                    if constexpr (ISUMS) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = m0 + 32 * a + c_row(r, lane), col = n0 + jl;
-                            if (row < M && col < N)
-                                S[((size_t)row * N + col) * nc + sb * 8 + c] = F[r] - MAGIC_BITS;
-                        }
-                    } else {
-                        const floatx4* dap = reinterpret_cast<const floatx4*>(&sm.ada[c][a][hg][0]);
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const floatx4 da = dap[q4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const int r = 4 * q4 + e;
-                                const float ev = fmaf(__int_as_float(F[r]), dsv, c0);   // dsv * I
-                                y[a][r] = fmaf(ev, da[e], y[a][r]);
-                            }
-                        }
-                    }
+                    for (int q4 = 0; q4 < 4; ++q4) dsv[q4] = dsvp[q4];
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (k1 < 16)
+                F[k1 & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, c1), bn, magic, 0, 0, 0);
+            const int32x16 Fk = F[k & 1];
+            if constexpr (ISUMS) {
+                const int tok = m0 + tk[ts];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = n0 + 32 * wave + c_row(r, lane);
+                    if (tok < M && row < N)
+                        S[((size_t)tok * N + row) * nc + sb * 8 + c] = Fk[r] - MAGIC_BITS;
+                }
+            } else {
+                const floatx4 dc = *reinterpret_cast<const floatx4*>(sm.ada + tk[ts] * DA_STRIDE + 4 * (c >> 1));
+                const float da = dc[c & 1], c0 = dc[2 + (c & 1)];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 4 * q4 + e;
+                        const float ev = fmaf(__int_as_float(Fk[r]), da, c0);       // round(da * I)
+                        y[ts][r] = fmaf(ev, dsv[q4][e], y[ts][r]);
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+
+        // ---------------- min term on the matrix core, accumulated into y
         if constexpr (!ISUMS) {
-            bf16x8 mB, mB2;
-            const int32x4 mraw = *reinterpret_cast<const int32x4*>(sm.bs + jl * BS_STRIDE + 64);
-            const int32x4 zero4 = {0, 0, 0, 0};
-            const int32x4 mraw2 = hg ? zero4 : mraw;
-            __builtin_memcpy(&mB, &mraw, 16);
-            __builtin_memcpy(&mB2, &mraw2, 16);
-            const float nd = sm.bnd[jl];
+            // k-slot groups per MFMA (lanes hg = 0 / 1): (w1,x1 | w1,x2), (w2,x1 | w1,x3), (w3,x1 | w2,x2)
+            const int wp0 = 0, wp1 = hg ? 0 : 1, wp2 = hg ? 1 : 2;
+            const int xp0 = hg ? 1 : 0, xp1 = hg ? 2 : 0, xp2 = hg ? 1 : 0;
+            const uint16_t* bwr = sm.bw + wr * PC_STRIDE;
+            bf16x8 wA0, wA1, wA2;
+            __builtin_memcpy(&wA0, bwr + 8 * wp0, 16);
+            __builtin_memcpy(&wA1, bwr + 8 * wp1, 16);
+            __builtin_memcpy(&wA2, bwr + 8 * wp2, 16);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                bf16x8 x12, x3;
-                __builtin_memcpy(&x12, sm.ax + (32 * a + l32) * AX_STRIDE + 16 * hg, 16);
-                __builtin_memcpy(&x3, sm.ax + (32 * a + l32) * AX_STRIDE + 32, 16);
-                floatx16 R;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) R[r] = 0.0f;
-                // k-group 0 carries x1, k-group 1 carries x2 (against m in both groups);
-                // then x3 against m in group 0 only.
-                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x12, mB, R, 0, 0, 0);
-                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x3, mB2, R, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) y[a][r] = fmaf(R[r], nd, y[a][r]);
+            for (int ts = 0; ts < 2; ++ts) {
+                const uint16_t* axr = sm.ax + tk[ts] * PC_STRIDE;
+                bf16x8 xB0, xB1, xB2;
+                __builtin_memcpy(&xB0, axr + 8 * xp0, 16);
+                __builtin_memcpy(&xB1, axr + 8 * xp1, 16);
+                __builtin_memcpy(&xB2, axr + 8 * xp2, 16);
+                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA0, xB0, y[ts], 0, 0, 0);
+                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA1, xB1, y[ts], 0, 0, 0);
+                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA2, xB2, y[ts], 0, 0, 0);
             }
         }
         __syncthreads();
     }
 
     if constexpr (!ISUMS) {
-        const int col = n0 + jl;
-        if (col < N) {
+        // lane (ts, l32) holds token m0 + 32ts + l32; register group b = r>>2 holds the four
+        // consecutive weight rows n0 + 32*wave + 8b + 4hg + 0..3
+        const bool vec = ((N & 3) == 0) && ((((uintptr_t)Y) & 15) == 0);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+        for (int ts = 0; ts < 2; ++ts) {
+            const int tok = m0 + tk[ts];
+            if (tok >= M) continue;
+            float* yrow = Y + (size_t)tok * N;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + 32 * a + c_row(r, lane);
-                    if (row < M) Y[(size_t)row * N + col] = y[a][r];
+            for (int b = 0; b < 4; ++b) {
+                const int row = n0 + 32 * wave + 8 * b + 4 * hg;
+                if (vec && row + 3 < N) {
+                    floatx4 v = {y[ts][4 * b], y[ts][4 * b + 1], y[ts][4 * b + 2], y[ts][4 * b + 3]};
+                    *reinterpret_cast<floatx4*>(yrow + row) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row + e < N) yrow[row + e] = y[ts][4 * b + e];
                 }
+            }
         }
     }
 }
