@@ -28,11 +28,13 @@
 //    y = fma(e, dsv, y) accumulates: two VALU ops per output per chunk, nothing else.
 //    MFMAs are issued one step ahead of the fold that consumes them, so the matrix core
 //    runs while the VALU folds the previous result.
-//  * Min term, entirely on the matrix core: per super-block, sum_s dmv_js * (da*ssum)_is
-//    is a K=8 product. Both factors are exact f32 (17 and 23 significant bits); each is
-//    split into three bf16 pieces that sum to it exactly, and three
-//    v_mfma_f32_32x32x16_bf16 accumulate the six significant piece products
-//    (w1x1 w1x2 w2x1 w1x3 w3x1 w2x2, dropped terms < 2^-23 relative) straight into y.
+//  * Min term: per super-block, sum_s m_js * (da*ssum)_is is a K=8 product. m (0..63) is
+//    exact in bf16; da*ssum is an exact f32 (11 + 12 significant bits) split into three
+//    bf16 pieces that sum to it exactly. Two v_mfma_f32_32x32x16_bf16 (pieces x1|x2 in the
+//    two k-groups, then x3 with the second group zeroed) give R with f32 accumulation, and
+//    one FMA with -dmin per output and super-block folds it into y. (On gfx950 matrix-core
+//    and VALU time add up, so this two-MFMA form is cheaper than carrying -dmin*m through
+//    more MFMAs.)
 //  * The "isums" instantiation runs the same staging, unpack and MFMA code and stores the
 //    integer sums instead of folding them (the bit-exact witness of the integer stage).
 #include "qpg_common.h"
@@ -45,7 +47,7 @@ typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
 constexpr int TM = 64;            // tokens per workgroup tile
 constexpr int TN = 128;           // weight rows per workgroup tile
 constexpr int DA_STRIDE = 20;     // floats per token: per chunk pair p: da_2p, da_2p+1, c0_2p, c0_2p+1 (+pad)
-constexpr int PC_STRIDE = 24;     // bf16 per token / row: three pieces x 8 sub-blocks
+constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks (per row: m x 8)
 
 struct alignas(16) Smem {
     alignas(16) uint8_t aq[TM * 256];          // q8 tile, granule g of token t at 16*(g ^ (t & 15))
@@ -53,7 +55,8 @@ struct alignas(16) Smem {
     alignas(16) float bdsv[8][TN];             // d*sc per chunk, rows in C-register order per wave
     alignas(16) float ada[TM * DA_STRIDE];     // da and -1.5*2^23*da per token and chunk
     alignas(16) uint16_t ax[TM * PC_STRIDE];   // bf16 pieces of da*ssum per token
-    alignas(16) uint16_t bw[TN * PC_STRIDE];   // bf16 pieces of -dmin*m per row
+    alignas(16) uint16_t bw[TN * PC_STRIDE];   // m per row and sub-block as bf16 (slots 0..7)
+    alignas(16) float bnd[TN];                 // -dmin per row, rows in C-register order per wave
 };
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
@@ -165,6 +168,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             const float dmin = half_bits_to_float((uint32_t)hv[0] >> 16);
             const uint32_t S0 = (uint32_t)hv[1], S1 = (uint32_t)hv[2], S2 = (uint32_t)hv[3];
             const int pos = 32 * (j >> 5) + c_pos(j & 31);
+            sm.bnd[pos] = -dmin;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 uint32_t sc, m;
@@ -177,7 +181,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                     m = ((S2 >> s4) >> 4 & 15u) | (((S1 >> s4) >> 6 & 3u) << 4);
                 }
                 sm.bdsv[s][pos] = d * (float)sc;                      // exact (17 bits)
-                split3_bf16(-(dmin * (float)m), sm.bw + j * PC_STRIDE + s, 8);   // exact (17 bits)
+                sm.bw[j * PC_STRIDE + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
             }
         }
         __syncthreads();
@@ -247,26 +251,32 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // ---------------- min term on the matrix core, accumulated into y
+        // ---------------- min term: R = sum_s m_s * (x1 + x2 + x3)_s on the matrix core, then
+        // y += -dmin * R. MFMA 1 pairs x1 (k-group 0) and x2 (k-group 1) with m, MFMA 2 pairs x3
+        // with m in k-group 0 only.
         if constexpr (!ISUMS) {
-            // k-slot groups per MFMA (lanes hg = 0 / 1): (w1,x1 | w1,x2), (w2,x1 | w1,x3), (w3,x1 | w2,x2)
-            const int wp0 = 0, wp1 = hg ? 0 : 1, wp2 = hg ? 1 : 2;
-            const int xp0 = hg ? 1 : 0, xp1 = hg ? 2 : 0, xp2 = hg ? 1 : 0;
-            const uint16_t* bwr = sm.bw + wr * PC_STRIDE;
-            bf16x8 wA0, wA1, wA2;
-            __builtin_memcpy(&wA0, bwr + 8 * wp0, 16);
-            __builtin_memcpy(&wA1, bwr + 8 * wp1, 16);
-            __builtin_memcpy(&wA2, bwr + 8 * wp2, 16);
+            const uint16_t* bwr = sm.bw + wr * PC_STRIDE;       // m of this lane's weight row
+            bf16x8 mA, mA2;
+            __builtin_memcpy(&mA, bwr, 16);
+            const int32x4 z4 = {0, 0, 0, 0};
+            int32x4 mraw; __builtin_memcpy(&mraw, bwr, 16);
+            const int32x4 mraw2 = hg ? z4 : mraw;
+            __builtin_memcpy(&mA2, &mraw2, 16);
+            floatx4 ndv[4];
+            const floatx4* ndp = reinterpret_cast<const floatx4*>(&sm.bnd[32 * wave + 16 * hg]);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) ndv[q4] = ndp[q4];
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
                 const uint16_t* axr = sm.ax + tk[ts] * PC_STRIDE;
-                bf16x8 xB0, xB1, xB2;
-                __builtin_memcpy(&xB0, axr + 8 * xp0, 16);
-                __builtin_memcpy(&xB1, axr + 8 * xp1, 16);
-                __builtin_memcpy(&xB2, axr + 8 * xp2, 16);
-                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA0, xB0, y[ts], 0, 0, 0);
-                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA1, xB1, y[ts], 0, 0, 0);
-                y[ts] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wA2, xB2, y[ts], 0, 0, 0);
+                bf16x8 x12, x3;
+                __builtin_memcpy(&x12, axr + 8 * hg, 16);
+                __builtin_memcpy(&x3, axr + 16, 16);
+                floatx16 R = {};
+                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA, x12, R, 0, 0, 0);
+                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA2, x3, R, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) y[ts][r] = fmaf(R[r], ndv[r >> 2][r & 3], y[ts][r]);
             }
         }
         __syncthreads();
