@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 METRIC = "int8 TMAC/s of q4_K/q6_K MMQ at 7B prefill shapes (M=512); % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s (2 ops per MAC)
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mmq_q4K_512x11008x4096.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mmq_q4K_512x11008x4096.txt")
 KERNEL_SOURCES = ["quantized_prefill_gemm_amd/csrc/mmq_q4k.hip", "quantized_prefill_gemm_amd/csrc/qpg_common.h"]
 
 
