@@ -3,25 +3,26 @@
 // Y[i][j] = sum over 16-wide sub-blocks u of da_{i,u/2} * (d*sc)_{ju} * J_iju,
 //   J_iju = sum_{k in u} (q6_jk - 32) * q_ik  (exact int32).
 // q6_K carries one int8 scale per 16 weights, so each 32-wide q8_1 chunk holds two
-// integer products with different scales -- the "KSPLIT=2" structure of the q6_K kernel
-// of "r40 - __launch_bounds__(256,3) third resident block" (sec. 5): two 16-k products
-// per chunk.
+// integer products with different scales -- the two 16-k products per 32-k chunk of the
+// q6_K kernel of "r40 - __launch_bounds__(256,3) third resident block" (sec. 5).
 //
 // MI355X design:
-//  * Same tile as the q4_K kernel (64 tokens x 128 weight rows, 4 waves, each wave 32
-//    weight rows x 64 tokens = two 32x32 sub-tiles).
-//  * Integer stage: v_mfma_i32_32x32x16_i8 per (sub-tile, 16-wide sub-block). The B
-//    operand is the unsigned 6-bit value q6 = low4 | high2 << 4 (0..63, a valid int8);
-//    the "- 32" is applied by the matrix core itself: a first MFMA multiplies the
-//    activations by a constant -32 operand onto the bits of 1.5*2^23, the second adds
-//    q6 * q onto that, so the int32 result read as f32 is 1.5*2^23 + J exactly
-//    (|J| <= 32*127*16 < 2^22) with no per-byte VALU work for the offset.
-//  * Fold: e = fma(F, d*sc, -1.5*2^23*d*sc) = round(d*sc*J); y = fma(e, da, y).
-//  * q6_K rows start only 2-byte aligned (210-byte blocks), so the staging reads aligned
-//    dwords and shifts them into place with v_alignbyte (no misaligned wide loads).
-//  * LDS layout: inside every 32-byte group of q, ql and qh, the 8-byte pieces 1 and 2
-//    are swapped at staging, so one 16-byte LDS read gives a lane its 8 bytes of both
-//    16-wide sub-blocks of a chunk (k-group l>>5 of each K=16 MFMA).
+//  * Tile 64 tokens x 128 weight rows, 4 waves; wave w = weight rows 32w..32w+31 (MFMA row
+//    side) x 64 tokens (two 32x32 sub-tiles on the column side): da is one value per lane,
+//    d*sc is read once per sub-block for both token sub-tiles.
+//  * Integer stage: v_mfma_i32_32x32x16_i8 per (token sub-tile, 16-wide sub-block). The
+//    weight operand v = q6 - 32 is assembled per byte in registers from the raw ql / qh bytes
+//    in LDS: q6 = low4 | high2 << 4, and v = ((q6 | 0x80) - 0x20) ^ 0x80 turns the unsigned
+//    6-bit value into the signed int8 q6 - 32 without any borrow between bytes.
+//  * The MFMA accumulates onto the bits of 1.5*2^23, so its int32 result read as f32 is
+//    1.5*2^23 + J exactly (|J| <= 32*127*16 < 2^22): e = fma(F, da, -1.5*2^23*da) is
+//    round(da*J) and y = fma(e, d*sc, y). Two VALU ops per output and sub-block.
+//  * q6_K rows start only 2-byte aligned (210-byte blocks): staging reads aligned dwords and
+//    shifts them into place with v_alignbyte, never a misaligned wide load.
+//  * LDS: inside every 32-byte group of q, ql and qh the 8-byte pieces 1 and 2 are swapped at
+//    staging, so one 16-byte read gives a lane its 8 bytes of both sub-blocks of a chunk
+//    (k-group l>>5 of each K=16 MFMA). Rows are XOR-swizzled in 16-byte granules so reads of
+//    16 consecutive rows hit 16 distinct bank groups.
 #include "qpg_common.h"
 
 namespace qpg {
@@ -32,21 +33,20 @@ typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 64;
 constexpr int TN = 128;
-constexpr int AQ_STRIDE = 272;    // q tile row (256 + 16 pad)
-constexpr int BL_STRIDE = 144;    // ql row (128 + 16 pad)
-constexpr int BH_STRIDE = 80;     // qh row (64 + 16 pad)
-constexpr int BS_STRIDE = 80;     // d*sc[16] f32 (64 + 16 pad)
+constexpr int DA_STRIDE = 20;     // floats per token: per chunk pair p: da_2p, da_2p+1, c0_2p, c0_2p+1 (+pad)
 
 struct alignas(16) Smem {
-    alignas(16) uint8_t aq[TM * AQ_STRIDE];
-    alignas(16) float ada[8][2][2][16];
-    alignas(16) uint8_t bl[TN * BL_STRIDE];
-    alignas(16) uint8_t bh[TN * BH_STRIDE];
-    alignas(16) uint8_t bs[TN * BS_STRIDE];
+    alignas(16) uint8_t aq[TM * 256];          // q8 tile, permuted pieces, granule g of token t at g ^ (t & 15)
+    alignas(16) uint8_t bl[TN * 128];          // ql, permuted pieces, granule g of row j at g ^ ((j >> 1) & 7)
+    alignas(16) uint8_t bh[TN * 64];           // qh, permuted pieces, granule g of row j at g ^ ((j >> 2) & 3)
+    alignas(16) float bdsc[16][TN];            // d*sc per sub-block, rows in C-register order per wave
+    alignas(16) float ada[TM * DA_STRIDE];     // da and -1.5*2^23*da per token and chunk
 };
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
 {
+    // round-robin XCD dispatch: give each XCD a contiguous range of tiles, M fastest, so
+    // the workgroups sharing a weight tile run on one XCD (one L2)
     const int bid = blockIdx.x;
     const int xcd = bid & 7, k = bid >> 3;
     const int q = total >> 3, r = total & 7;
@@ -55,13 +55,15 @@ __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_
     n_tile = t / tiles_m;
 }
 
+__device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
+
 __device__ __forceinline__ uint32_t ld32(const uint8_t* p)
 {
     return *reinterpret_cast<const uint32_t*>(p);     // p is 4-byte aligned
 }
 
-// 16 bytes starting at the 2-byte aligned address base + off, read as aligned dwords
-// from [base + off - sh, base + off - sh + 16 + 4*(sh != 0)).
+// 16 bytes starting at the 2-byte aligned address p, read as aligned dwords from
+// [p - sh, p - sh + 16 + 4*(sh != 0)), sh = p & 2.
 __device__ __forceinline__ uint32x4 ld16_a2(const uint8_t* p, uint32_t sh)
 {
     const uint8_t* a = p - sh;
@@ -79,60 +81,72 @@ __device__ __forceinline__ uint32x4 ld16_a2(const uint8_t* p, uint32_t sh)
     return v;
 }
 
-// Store a 16-byte granule that sits at byte 16*gi (gi = 0/1) of a 32-byte group into the
-// permuted group: bytes 0-7 go to 8*gi, bytes 8-15 to 16 + 8*gi.
-__device__ __forceinline__ void st_perm(uint8_t* group, int gi, uint32x4 v)
+// A 16-byte granule at byte 16*gi (gi = 0/1) of a 32-byte group, stored with the group's
+// pieces 1 and 2 swapped: bytes 0-7 go to piece gi, bytes 8-15 to piece 2 + gi. `grp` is the
+// group's LDS base; the pieces land in granules (2*G + 0/1) ^ sw of the row.
+__device__ __forceinline__ void st_perm(uint8_t* row, int G, int gi, int sw, uint32x4 v)
 {
-    uint32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-    *reinterpret_cast<uint32x2*>(group + 8 * gi) = lo;
-    *reinterpret_cast<uint32x2*>(group + 16 + 8 * gi) = hi;
+    const uint32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
+    // piece P (0..3) of group G sits in granule 2G + (P >> 1), half (P & 1)
+    *reinterpret_cast<uint32x2*>(row + 16 * ((2 * G + 0) ^ sw) + 8 * gi) = lo;   // piece gi
+    *reinterpret_cast<uint32x2*>(row + 16 * ((2 * G + 1) ^ sw) + 8 * gi) = hi;   // piece 2 + gi
 }
 
 template <bool ISUMS>
-__global__ void __launch_bounds__(256) mmq_q6K_kernel(const uint8_t* __restrict__ W,
-                                                      const int8_t* __restrict__ qplane,
-                                                      const uint32_t* __restrict__ hdr,
-                                                      float* __restrict__ Y,
-                                                      int32_t* __restrict__ S,
-                                                      int M, int N, int K, int tiles_m, int total)
+__global__ void __launch_bounds__(256, ISUMS ? 1 : 2) mmq_q6K_kernel(const uint8_t* __restrict__ W,
+                                                                     const int8_t* __restrict__ qplane,
+                                                                     const uint32_t* __restrict__ hdr,
+                                                                     float* __restrict__ Y,
+                                                                     int32_t* __restrict__ S,
+                                                                     int M, int N, int K, int tiles_m, int total)
 {
     __shared__ Smem sm;
     int m_tile, n_tile;
     tile_coords(m_tile, n_tile, tiles_m, total);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = lane >> 5, l32 = lane & 31;
     const int m0 = m_tile * TM, n0 = n_tile * TN;
     const int nsb = K / QK_K, nc = K / QK8, nu = K / 16;
     const size_t wrow = (size_t)nsb * Q6K_BYTES;
-    const int jl = 32 * wave + l32;
+
+    const int rows_t = min(TM, M - m0);
+    const __amdgpu_buffer_rsrc_t rQ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qplane + (size_t)m0 * K), 0, rows_t * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
     int32x16 magic;
 #pragma unroll
     for (int r = 0; r < 16; ++r) magic[r] = MAGIC_BITS;
-    const long minus32 = (long)0xE0E0E0E0E0E0E0E0ull;     // eight int8 -32
     floatx16 y[2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
+    const int wr = 32 * wave + l32;                  // weight row of this lane's A operand
+    int tk[2];
+#pragma unroll
+    for (int ts = 0; ts < 2; ++ts) tk[ts] = 32 * ts + l32;
+
     for (int sb = 0; sb < nsb; ++sb) {
-        // ---------------- stage A: q8 tile, 16-byte granule p of a row is sub-block p
+        // ---------------- stage A: q8 tile; 16-byte granule p of a row is sub-block p
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int g = it * 256 + tid, t = g >> 4, part = g & 15;
-            uint32x4 v = {0u, 0u, 0u, 0u};
-            if (m0 + t < M)
-                v = *reinterpret_cast<const uint32x4*>(qplane + (size_t)(m0 + t) * K + sb * QK_K + part * 16);
-            st_perm(sm.aq + t * AQ_STRIDE + 32 * (part >> 1), part & 1, v);
+            const uint32x4 v = __builtin_bit_cast(
+                uint32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, t * K + sb * QK_K + part * 16, 0, 0));
+            st_perm(sm.aq + t * 256, part >> 1, part & 1, t & 15, v);
         }
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int h = it * 256 + tid, t = h >> 3, c = h & 7;
-            uint32_t hw = 0;
-            if (m0 + t < M) hw = hdr[(size_t)(m0 + t) * nc + sb * 8 + c];
-            const int a = t >> 5, tt = t & 31;
-            sm.ada[c][a][(tt >> 2) & 1][4 * (tt >> 3) + (tt & 3)] = half_bits_to_float(hw & 0xFFFFu);
+            const uint32_t hw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rH, (t * nc + sb * 8 + c) * 4, 0, 0);
+            const float da = half_bits_to_float(hw & 0xFFFFu);
+            float* ad = sm.ada + t * DA_STRIDE + 4 * (c >> 1) + (c & 1);
+            ad[0] = da;
+            ad[2] = -MAGIC_F * da;                                                  // exact
         }
         // ---------------- stage B: ql (8 granules) and qh (4 granules) per row
 #pragma unroll
@@ -144,87 +158,93 @@ __global__ void __launch_bounds__(256) mmq_q6K_kernel(const uint8_t* __restrict_
                 v = ld16_a2(W + off + 16 * gi, (uint32_t)(off & 2));
             }
             if (gi < 8)
-                st_perm(sm.bl + j * BL_STRIDE + 32 * (gi >> 1), gi & 1, v);
+                st_perm(sm.bl + j * 128, gi >> 1, gi & 1, (j >> 1) & 7, v);
             else
-                st_perm(sm.bh + j * BH_STRIDE + 32 * ((gi - 8) >> 1), gi & 1, v);
+                st_perm(sm.bh + j * 64, (gi - 8) >> 1, gi & 1, (j >> 2) & 3, v);
         }
-        // ---------------- stage B: d * sc[u] per row
+        // ---------------- stage B: d * sc[u] per row, in C-register order
         if (tid < TN) {
             const int j = tid;
-            float* bs = reinterpret_cast<float*>(sm.bs + j * BS_STRIDE);
+            const int pos = 32 * (j >> 5) + c_pos(j & 31);
             if (n0 + j < N) {
                 const size_t off = (size_t)(n0 + j) * wrow + (size_t)sb * Q6K_BYTES;
-                const uint32_t sh = (uint32_t)(off & 2);
-                const uint32x4 scw = ld16_a2(W + off + 192, sh);
-                const uint32_t dbits = *reinterpret_cast<const uint16_t*>(W + off + 208);
-                const float d = half_bits_to_float(dbits);
+                const uint32x4 scw = ld16_a2(W + off + 192, (uint32_t)(off & 2));
+                const float d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(W + off + 208));
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
-                    const int sc = (int)(int8_t)(scw[u >> 2] >> (8 * (u & 3)));
-                    bs[u] = d * (float)sc;                          // exact (19 bits)
-                }
+                for (int u = 0; u < 16; ++u)
+                    sm.bdsc[u][pos] = d * (float)(int)(int8_t)(scw[u >> 2] >> (8 * (u & 3)));   // exact
             } else {
 #pragma unroll
-                for (int u = 0; u < 16; ++u) bs[u] = 0.0f;
+                for (int u = 0; u < 16; ++u) sm.bdsc[u][pos] = 0.0f;
             }
         }
         __syncthreads();
 
-        // ---------------- compute
-        const floatx4* bsp = reinterpret_cast<const floatx4*>(sm.bs + jl * BS_STRIDE);
-        floatx4 dsc4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dsc4[i] = bsp[i];
+        // ---------------- integer stage + fold
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) {
+            // keep each chunk's loads and products together: bounds the live registers to one
+            // chunk's operands. (Two resident workgroups per CU: at three the 168-register budget
+            // spills, and the spilling form measured 1.6x slower.)
+            __builtin_amdgcn_sched_barrier(0);
             const int h = cc >> 2, g = cc & 3;
-            const uint32x4 ql = *reinterpret_cast<const uint32x4*>(sm.bl + jl * BL_STRIDE + 64 * h + 32 * (g & 1) + 16 * hg);
-            const uint32x4 qh = *reinterpret_cast<const uint32x4*>(sm.bh + jl * BH_STRIDE + 32 * h + 16 * hg);
-            uint32x4 q6;
+            // weight operand for both sub-blocks of the chunk: 16 bytes of ql and of qh
+            const uint32x4 ql = *reinterpret_cast<const uint32x4*>(
+                sm.bl + wr * 128 + 16 * ((4 * h + 2 * (g & 1) + hg) ^ ((wr >> 1) & 7)));
+            const uint32x4 qh = *reinterpret_cast<const uint32x4*>(
+                sm.bh + wr * 64 + 16 * ((2 * h + hg) ^ ((wr >> 2) & 3)));
+            uint32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t lo = (ql[e] >> (4 * (g >> 1))) & 0x0F0F0F0Fu;
                 const uint32_t hi = ((qh[e] >> (2 * g)) & 0x03030303u) << 4;
-                q6[e] = lo | hi;
+                const uint32_t q6 = lo | hi | 0x80808080u;                  // bit 7 set: no borrow below
+                v[e] = (q6 - 0x20202020u) ^ 0x80808080u;                    // signed q6 - 32 per byte
             }
-            const long b0 = (long)(((unsigned long)q6[1] << 32) | q6[0]);
-            const long b1 = (long)(((unsigned long)q6[3] << 32) | q6[2]);
+            const long a0 = (long)(((unsigned long)v[1] << 32) | v[0]);    // sub-block 2cc, k-group hg
+            const long a1 = (long)(((unsigned long)v[3] << 32) | v[2]);    // sub-block 2cc+1
+            floatx4 s0[4], s1[4];
+            if constexpr (!ISUMS) {
+                const floatx4* p0 = reinterpret_cast<const floatx4*>(&sm.bdsc[2 * cc][32 * wave + 16 * hg]);
+                const floatx4* p1 = reinterpret_cast<const floatx4*>(&sm.bdsc[2 * cc + 1][32 * wave + 16 * hg]);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const uint32x4 av =
-                    *reinterpret_cast<const uint32x4*>(sm.aq + (32 * a + l32) * AQ_STRIDE + 32 * cc + 16 * hg);
-                const long a0 = (long)(((unsigned long)av[1] << 32) | av[0]);
-                const long a1 = (long)(((unsigned long)av[3] << 32) | av[2]);
-                int32x16 F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, minus32, magic, 0, 0, 0);
-                F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, F0, 0, 0, 0);
-                int32x16 F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, minus32, magic, 0, 0, 0);
-                F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, b1, F1, 0, 0, 0);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    s0[q4] = p0[q4];
+                    s1[q4] = p1[q4];
+                }
+            }
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts) {
+                const uint32x4 bq = *reinterpret_cast<const uint32x4*>(
+                    sm.aq + tk[ts] * 256 + 16 * ((2 * cc + hg) ^ (tk[ts] & 15)));
+                const long b0 = (long)(((unsigned long)bq[1] << 32) | bq[0]);
+                const long b1 = (long)(((unsigned long)bq[3] << 32) | bq[2]);
+                const int32x16 F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, magic, 0, 0, 0);
+                const int32x16 F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, b1, magic, 0, 0, 0);
                 if constexpr (ISUMS) {
+                    const int tok = m0 + tk[ts];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = m0 + 32 * a + c_row(r, lane), col = n0 + jl;
-                        if (row < M && col < N) {
-                            int32_t* dst = S + ((size_t)row * N + col) * nu + sb * 16 + 2 * cc;
+                        const int row = n0 + 32 * wave + c_row(r, lane);
+                        if (tok < M && row < N) {
+                            int32_t* dst = S + ((size_t)tok * N + row) * nu + sb * 16 + 2 * cc;
                             dst[0] = F0[r] - MAGIC_BITS;
                             dst[1] = F1[r] - MAGIC_BITS;
                         }
                     }
                 } else {
-                    const float s0 = dsc4[(2 * cc) >> 2][(2 * cc) & 3];
-                    const float s1 = dsc4[(2 * cc + 1) >> 2][(2 * cc + 1) & 3];
-                    const float c00 = -MAGIC_F * s0, c01 = -MAGIC_F * s1;
-                    const floatx4* dap = reinterpret_cast<const floatx4*>(&sm.ada[cc][a][hg][0]);
+                    const floatx4 dc = *reinterpret_cast<const floatx4*>(sm.ada + tk[ts] * DA_STRIDE + 4 * (cc >> 1));
+                    const float da = dc[cc & 1], c0 = dc[2 + (cc & 1)];
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const floatx4 da = dap[q4];
+                    for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int r = 4 * q4 + e;
-                            const float e0 = fmaf(__int_as_float(F0[r]), s0, c00);
-                            const float e1 = fmaf(__int_as_float(F1[r]), s1, c01);
-                            y[a][r] = fmaf(e0 + e1, da[e], y[a][r]);
+                            const float e0 = fmaf(__int_as_float(F0[r]), da, c0);    // round(da * J0)
+                            const float e1 = fmaf(__int_as_float(F1[r]), da, c0);    // round(da * J1)
+                            y[ts][r] = fmaf(e0, s0[q4][e], y[ts][r]);
+                            y[ts][r] = fmaf(e1, s1[q4][e], y[ts][r]);
                         }
-                    }
                 }
             }
         }
@@ -232,15 +252,26 @@ __global__ void __launch_bounds__(256) mmq_q6K_kernel(const uint8_t* __restrict_
     }
 
     if constexpr (!ISUMS) {
-        const int col = n0 + jl;
-        if (col < N) {
+        // lane (ts, l32) holds token m0 + 32ts + l32; register group b = r>>2 holds the four
+        // consecutive weight rows n0 + 32*wave + 8b + 4hg + 0..3
+        const bool vec = ((N & 3) == 0) && ((((uintptr_t)Y) & 15) == 0);
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+        for (int ts = 0; ts < 2; ++ts) {
+            const int tok = m0 + tk[ts];
+            if (tok >= M) continue;
+            float* yrow = Y + (size_t)tok * N;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + 32 * a + c_row(r, lane);
-                    if (row < M) Y[(size_t)row * N + col] = y[a][r];
+            for (int b = 0; b < 4; ++b) {
+                const int row = n0 + 32 * wave + 8 * b + 4 * hg;
+                if (vec && row + 3 < N) {
+                    floatx4 v = {y[ts][4 * b], y[ts][4 * b + 1], y[ts][4 * b + 2], y[ts][4 * b + 3]};
+                    *reinterpret_cast<floatx4*>(yrow + row) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (row + e < N) yrow[row + e] = y[ts][4 * b + e];
                 }
+            }
         }
     }
 }
