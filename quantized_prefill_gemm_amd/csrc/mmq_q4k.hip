@@ -14,10 +14,16 @@
 //    the MFMA row side and the tokens on the column side, so each lane's 16 accumulators
 //    share one token: da is one register per lane, the per-row d*sc is read once per
 //    chunk and serves both token sub-tiles.
-//  * Per super-block (256 k) the workgroup stages, with 16-byte buffer loads (hardware
-//    range checks give zeros past the last token / row, no branches), the raw qs bytes
-//    (128 B per row) and the q8_1 int8 tile into XOR-swizzled LDS, and decodes the block
-//    headers once into per-(row, sub-block) f32 terms.
+//  * Staging is a two-deep pipeline of half super-blocks (128 k: 8 KiB of q8 tile, 8 KiB
+//    of raw qs) moved by LDS-direct buffer loads (buffer_load_dwordx4 ... lds): the loads
+//    of stage h+1 are issued before stage h is computed, land in LDS without passing
+//    through registers, and are waited for only at the next stage boundary. Each lane
+//    fetches the 16-byte granule that belongs at its LDS slot; rows are padded to an odd
+//    number of 16-byte slots (bank spread), pad slots are filled from an out-of-range
+//    offset (zeros), and so are tokens / rows past the end of the matrix. The block
+//    headers (q8_1 words, q4_K d/dmin/scales) are loaded into registers one super-block
+//    ahead and decoded once per super-block into per-(row, sub-block) and per-(token,
+//    chunk) f32 terms.
 //  * Integer stage: one v_mfma_i32_32x32x32_i8 per (sub-tile, chunk). K = 32 is exactly
 //    one q8_1 block and one q4_K sub-block, so no two scales share an integer
 //    accumulator. One 16-byte LDS read of raw qs serves two chunks: low nibbles
@@ -43,21 +49,33 @@ namespace qpg {
 namespace q4k {
 
 typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TM = 64;            // tokens per workgroup tile
 constexpr int TN = 128;           // weight rows per workgroup tile
-constexpr int DA_STRIDE = 20;     // floats per token: per chunk pair p: da_2p, da_2p+1, c0_2p, c0_2p+1 (+pad)
-constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks (per row: m x 8)
+constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks
+constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
 
-struct alignas(16) Smem {
-    alignas(16) uint8_t aq[TM * 256];          // q8 tile, granule g of token t at 16*(g ^ (t & 15))
-    alignas(16) uint8_t bq[TN * 128];          // raw qs, granule g of row j at 16*(g ^ ((j >> 1) & 7))
-    alignas(16) float bdsv[8][TN];             // d*sc per chunk, rows in C-register order per wave
-    alignas(16) float ada[TM * DA_STRIDE];     // da and -1.5*2^23*da per token and chunk
-    alignas(16) uint16_t ax[TM * PC_STRIDE];   // bf16 pieces of da*ssum per token
-    alignas(16) uint16_t bw[TN * PC_STRIDE];   // m per row and sub-block as bf16 (slots 0..7)
-    alignas(16) float bnd[TN];                 // -dmin per row, rows in C-register order per wave
-};
+// One LDS object per buffer, so the compiler can tell the stage being computed from the
+// one being loaded and does not make reads of the first wait for loads of the second.
+// Stage-buffer layouts, in 16-byte slots (a row pitch of 9 resp. 5 slots puts 16
+// consecutive tokens / rows of one ds_read_b128 phase on 16 distinct bank groups, and
+// every read address is one base register plus an immediate):
+//   q8 tile: token t, granule g (k 16g..16g+15 of the half) at slot 9t + g; slot 9t + 8 is pad
+//   raw qs:  row j, granule g (qs bytes 16g.. of the half)   at slot 5j + g; slot 5j + 4 is pad
+constexpr int AQ_SLOTS = TM * 9, BQ_SLOTS = TN * 5;          // 576 and 640: 9 and 10 slabs of 64
+__shared__ __attribute__((aligned(16))) uint8_t s_aq0[AQ_SLOTS * 16];
+__shared__ __attribute__((aligned(16))) uint8_t s_aq1[AQ_SLOTS * 16];
+__shared__ __attribute__((aligned(16))) uint8_t s_bq0[BQ_SLOTS * 16];
+__shared__ __attribute__((aligned(16))) uint8_t s_bq1[BQ_SLOTS * 16];
+__shared__ __attribute__((aligned(16))) float s_dsv[8][TN];           // d*sc per chunk, rows in C-register order per wave
+__shared__ __attribute__((aligned(16))) float2 s_ada[8][TM];          // (da, -1.5*2^23*da) per chunk and token
+__shared__ __attribute__((aligned(16))) uint16_t s_ax[TM * PC_STRIDE];  // bf16 pieces of da*ssum per token
+__shared__ __attribute__((aligned(16))) uint16_t s_bw[TN * 8];        // m per row and sub-block as bf16
+__shared__ __attribute__((aligned(16))) float s_bnd[TN];              // -dmin per row, rows in C-register order per wave
+
+// Source offset of a pad slot: past every buffer's range, so the load writes zeros.
+constexpr unsigned PAD_OFF = 0x7F000000u;
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
 {
@@ -89,6 +107,15 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t* dst, int stride)
     dst[2 * stride] = (uint16_t)b3;
 }
 
+// Wait until this wave's outstanding vector-memory operations (the LDS-direct loads) are
+// complete: vmcnt(0), expcnt and lgkmcnt left at their maxima.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voff, 0, 0, 0);
+}
+
 template <bool ISUMS>
 __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qplane,
@@ -97,10 +124,10 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                                                          int32_t* __restrict__ S,
                                                          int M, int N, int K, int tiles_m, int total)
 {
-    __shared__ Smem sm;
     int m_tile, n_tile;
     tile_coords(m_tile, n_tile, tiles_m, total);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = lane >> 5, l32 = lane & 31;
     const int m0 = m_tile * TM, n0 = n_tile * TN;
     const int nsb = K / QK_K, nc = K / QK8;
@@ -116,6 +143,45 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
     const __amdgpu_buffer_rsrc_t rH =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
+    // Per-lane source offsets of the LDS-direct loads. A slab is 64 consecutive slots
+    // (1 KiB) written by one wave instruction, lane L to slot 64*slab + L. The q8 tile has
+    // 9 slabs (wave w: slabs w, w+4, and 8 for wave 0), the raw qs 10 (wave w: w, w+4, and
+    // 8 + w for waves 0-1). Pad slots get PAD_OFF. Stage offsets are added per load.
+    const int nA = wave == 0 ? 3 : 2, nB = wave < 2 ? 3 : 2;
+    unsigned voA[3], voB[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int sa = 64 * (i < 2 ? wave + 4 * i : 8) + lane;
+        const int t = sa / 9, ga = sa - 9 * t;
+        voA[i] = ga == 8 ? PAD_OFF : (unsigned)(t * K + 16 * ga);
+        const int sbq = 64 * (i < 2 ? wave + 4 * i : 8 + wave) + lane;
+        const int j = sbq / 5, gb = sbq - 5 * j;
+        voB[i] = gb == 4 ? PAD_OFF : (unsigned)(j * wrow + 16 + 16 * gb);
+    }
+
+    auto issue_stage = [&](int sb, int hh, uint8_t* aq, uint8_t* bq) {
+        const unsigned oa = sb * QK_K + hh * HALF, ob = sb * Q4K_BYTES + hh * (HALF / 2);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+            if (i < nA) lds_load16(rQ, aq + 1024 * (i < 2 ? wave + 4 * i : 8), (int)(voA[i] + oa));
+            if (i < nB) lds_load16(rW, bq + 1024 * (i < 2 ? wave + 4 * i : 8 + wave), (int)(voB[i] + ob));
+        }
+    };
+
+    // Block headers of one super-block, one 16-byte load per thread into registers:
+    // threads 0..127 the q4_K header (d, dmin, 12 scale bytes) of row tid, threads
+    // 128..255 four q8_1 words (token (tid-128)/2, chunks 4*(tid&1)..+3).
+    auto load_headers = [&](int sb) -> uint32x4 {
+        int32x4 v;
+        if (tid < TN)
+            v = __builtin_amdgcn_raw_buffer_load_b128(rW, tid * wrow + sb * Q4K_BYTES, 0, 0);
+        else {
+            const int u = tid - TN;
+            v = __builtin_amdgcn_raw_buffer_load_b128(rH, ((u >> 1) * nc + sb * 8 + 4 * (u & 1)) * 4, 0, 0);
+        }
+        return __builtin_bit_cast(uint32x4, v);
+    };
+
     int32x16 magic;
 #pragma unroll
     for (int r = 0; r < 16; ++r) magic[r] = MAGIC_BITS;
@@ -126,49 +192,20 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
     const int wr = 32 * wave + l32;                 // weight row of this lane's A operand
-    const int wsw = (wr >> 1) & 7;                   // its LDS swizzle
-    int tk[2], tsw[2];
-#pragma unroll
-    for (int ts = 0; ts < 2; ++ts) {
-        tk[ts] = 32 * ts + l32;                      // token of this lane's B operand / outputs
-        tsw[ts] = tk[ts] & 15;
-    }
+    // Lane bases of the compute-phase reads (everything else is an immediate offset):
+    const int aq_base = 144 * l32 + 16 * hg;         // token l32 (+32 tokens = +4608), k-group hg
+    const int bq_base = 80 * wr + 16 * hg;           // row wr, k-group hg
 
-    for (int sb = 0; sb < nsb; ++sb) {
-        // ---------------- stage A: q8 tile (64 tokens x 256 B)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int g = it * 256 + tid, t = g >> 4, gi = g & 15;
-            const int32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rQ, t * K + sb * QK_K + gi * 16, 0, 0);
-            *reinterpret_cast<int32x4*>(sm.aq + t * 256 + 16 * (gi ^ (t & 15))) = v;
-        }
-        // ---------------- stage A: headers -> da, -1.5*2^23*da, bf16 pieces of da*ssum
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int h = it * 256 + tid, t = h >> 3, c = h & 7;
-            const uint32_t hw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rH, (t * nc + sb * 8 + c) * 4, 0, 0);
-            const float da = half_bits_to_float(hw & 0xFFFFu);
-            float* ad = sm.ada + t * DA_STRIDE + 4 * (c >> 1) + (c & 1);
-            ad[0] = da;
-            ad[2] = -MAGIC_F * da;                                  // exact
-            split3_bf16(da * (float)(int16_t)(hw >> 16), sm.ax + t * PC_STRIDE + c, 8);   // da*ssum exact
-        }
-        // ---------------- stage B: raw qs (128 rows x 128 B)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int g = it * 256 + tid, j = g >> 3, gi = g & 7;
-            const int32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rW, j * wrow + sb * Q4K_BYTES + 16 + gi * 16, 0, 0);
-            *reinterpret_cast<int32x4*>(sm.bq + j * 128 + 16 * (gi ^ ((j >> 1) & 7))) = v;
-        }
-        // ---------------- stage B: d, dmin and the eight 6-bit (sc, m) pairs of each row
+    // Decode one super-block's headers (held in registers by the thread that loaded them)
+    // into the fold terms.
+    auto decode_headers = [&](const uint32x4 hv) {
         if (tid < TN) {
             const int j = tid;
-            const int32x4 hv = __builtin_amdgcn_raw_buffer_load_b128(rW, j * wrow + sb * Q4K_BYTES, 0, 0);
-            const float d = half_bits_to_float((uint32_t)hv[0] & 0xFFFFu);
-            const float dmin = half_bits_to_float((uint32_t)hv[0] >> 16);
-            const uint32_t S0 = (uint32_t)hv[1], S1 = (uint32_t)hv[2], S2 = (uint32_t)hv[3];
+            const float d = half_bits_to_float(hv[0] & 0xFFFFu);
+            const float dmin = half_bits_to_float(hv[0] >> 16);
+            const uint32_t S0 = hv[1], S1 = hv[2], S2 = hv[3];
             const int pos = 32 * (j >> 5) + c_pos(j & 31);
-            sm.bnd[pos] = -dmin;
+            s_bnd[pos] = -dmin;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 uint32_t sc, m;
@@ -180,17 +217,25 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                     sc = ((S2 >> s4) & 15u) | (((S0 >> s4) >> 6 & 3u) << 4);
                     m = ((S2 >> s4) >> 4 & 15u) | (((S1 >> s4) >> 6 & 3u) << 4);
                 }
-                sm.bdsv[s][pos] = d * (float)sc;                      // exact (17 bits)
-                sm.bw[j * PC_STRIDE + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
+                s_dsv[s][pos] = d * (float)sc;                      // exact (17 bits)
+                s_bw[j * 8 + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
+            }
+        } else {
+            const int u = tid - TN, t = u >> 1, c4 = 4 * (u & 1);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = c4 + e;
+                const uint32_t hw = hv[e];
+                const float da = half_bits_to_float(hw & 0xFFFFu);
+                s_ada[c][t] = make_float2(da, -MAGIC_F * da);       // exact
+                split3_bf16(da * (float)(int16_t)(hw >> 16), s_ax + t * PC_STRIDE + c, 8);   // da*ssum exact
             }
         }
-        __syncthreads();
+    };
 
-        // ---------------- integer stage + fold, MFMA one step ahead of the fold
-        // Step k = 0..15 is (chunk c = k/2, token sub-tile ts = k%2). In step k the wave
-        // issues the LDS reads for step k+1, the MFMA of step k+1, then folds step k; the
-        // scheduling barriers keep that order, so only two accumulator blocks and one set
-        // of operands are live at a time.
+    // Integer stage + fold over the four chunks of one half super-block, MFMA one step
+    // ahead of the fold. Step k = 0..7 is (chunk c = 4*hh + k/2, token sub-tile k%2).
+    auto compute_stage = [&](int sb, int hh, const uint8_t* aq, const uint8_t* bq) {
         auto a_from = [&](const uint32x4& raw, int c) -> int32x4 {
             const uint32x4 u = (c & 1) ? ((raw >> 4u) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
             int32x4 r;
@@ -198,38 +243,37 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             return r;
         };
         auto ld_raw = [&](int p) -> uint32x4 {
-            return *reinterpret_cast<const uint32x4*>(sm.bq + wr * 128 + 16 * ((2 * p + hg) ^ wsw));
+            return *reinterpret_cast<const uint32x4*>(bq + bq_base + 32 * p);
         };
-        auto ld_b = [&](int c, int ts) -> int32x4 {
-            return *reinterpret_cast<const int32x4*>(sm.aq + tk[ts] * 256 + 16 * ((2 * c + hg) ^ tsw[ts]));
+        auto ld_b = [&](int cl, int ts) -> int32x4 {
+            return *reinterpret_cast<const int32x4*>(aq + aq_base + 4608 * ts + 32 * cl);
         };
-
         uint32x4 raw = ld_raw(0);
         int32x16 F[2];
         F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, 0), ld_b(0, 0), magic, 0, 0, 0);
         floatx4 dsv[4];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int c = k >> 1, ts = k & 1;
-            const int k1 = k + 1, c1 = k1 >> 1, ts1 = k1 & 1;
+        for (int k = 0; k < 8; ++k) {
+            const int cl = k >> 1, ts = k & 1, c = 4 * hh + cl;
+            const int k1 = k + 1, cl1 = k1 >> 1, ts1 = k1 & 1;
             int32x4 bn;
-            if (k1 < 16) {
+            if (k1 < 8) {
                 if ((k1 & 3) == 0) raw = ld_raw(k1 >> 2);
-                bn = ld_b(c1, ts1);
+                bn = ld_b(cl1, ts1);
             }
             if constexpr (!ISUMS) {
                 if (ts == 0) {
-                    const floatx4* dsvp = reinterpret_cast<const floatx4*>(&sm.bdsv[c][32 * wave + 16 * hg]);
+                    const floatx4* dsvp = reinterpret_cast<const floatx4*>(&s_dsv[c][32 * wave + 16 * hg]);
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) dsv[q4] = dsvp[q4];
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (k1 < 16)
-                F[k1 & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, c1), bn, magic, 0, 0, 0);
+            if (k1 < 8)
+                F[k1 & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, cl1), bn, magic, 0, 0, 0);
             const int32x16 Fk = F[k & 1];
             if constexpr (ISUMS) {
-                const int tok = m0 + tk[ts];
+                const int tok = m0 + 32 * ts + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = n0 + 32 * wave + c_row(r, lane);
@@ -237,8 +281,8 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                         S[((size_t)tok * N + row) * nc + sb * 8 + c] = Fk[r] - MAGIC_BITS;
                 }
             } else {
-                const floatx4 dc = *reinterpret_cast<const floatx4*>(sm.ada + tk[ts] * DA_STRIDE + 4 * (c >> 1));
-                const float da = dc[c & 1], c0 = dc[2 + (c & 1)];
+                const float2 dc = s_ada[c][32 * ts + l32];
+                const float da = dc.x, c0 = dc.y;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
@@ -250,36 +294,61 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // The folds of this stage are done here: without the pin, they may be sunk past the
+        // next barrier, which keeps all eight MFMA results live at once.
+        asm volatile("" : "+v"(y[0]), "+v"(y[1]));
+    };
 
-        // ---------------- min term: R = sum_s m_s * (x1 + x2 + x3)_s on the matrix core, then
-        // y += -dmin * R. MFMA 1 pairs x1 (k-group 0) and x2 (k-group 1) with m, MFMA 2 pairs x3
-        // with m in k-group 0 only.
-        if constexpr (!ISUMS) {
-            const uint16_t* bwr = sm.bw + wr * PC_STRIDE;       // m of this lane's weight row
-            bf16x8 mA, mA2;
-            __builtin_memcpy(&mA, bwr, 16);
-            const int32x4 z4 = {0, 0, 0, 0};
-            int32x4 mraw; __builtin_memcpy(&mraw, bwr, 16);
-            const int32x4 mraw2 = hg ? z4 : mraw;
-            __builtin_memcpy(&mA2, &mraw2, 16);
-            floatx4 ndv[4];
-            const floatx4* ndp = reinterpret_cast<const floatx4*>(&sm.bnd[32 * wave + 16 * hg]);
+    // Min term of one super-block: R = sum_s m_s * (x1 + x2 + x3)_s on the matrix core, then
+    // y += -dmin * R. MFMA 1 pairs x1 (k-group 0) and x2 (k-group 1) with m, MFMA 2 pairs x3
+    // with m in k-group 0 only.
+    auto min_term = [&]() {
+        const uint16_t* bwr = s_bw + wr * 8;            // m of this lane's weight row
+        bf16x8 mA, mA2;
+        __builtin_memcpy(&mA, bwr, 16);
+        const int32x4 z4 = {0, 0, 0, 0};
+        int32x4 mraw; __builtin_memcpy(&mraw, bwr, 16);
+        const int32x4 mraw2 = hg ? z4 : mraw;
+        __builtin_memcpy(&mA2, &mraw2, 16);
+        floatx4 ndv[4];
+        const floatx4* ndp = reinterpret_cast<const floatx4*>(&s_bnd[32 * wave + 16 * hg]);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) ndv[q4] = ndp[q4];
+        for (int q4 = 0; q4 < 4; ++q4) ndv[q4] = ndp[q4];
 #pragma unroll
-            for (int ts = 0; ts < 2; ++ts) {
-                const uint16_t* axr = sm.ax + tk[ts] * PC_STRIDE;
-                bf16x8 x12, x3;
-                __builtin_memcpy(&x12, axr + 8 * hg, 16);
-                __builtin_memcpy(&x3, axr + 16, 16);
-                floatx16 R = {};
-                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA, x12, R, 0, 0, 0);
-                R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA2, x3, R, 0, 0, 0);
+        for (int ts = 0; ts < 2; ++ts) {
+            const uint16_t* axr = s_ax + (32 * ts + l32) * PC_STRIDE;
+            bf16x8 x12, x3;
+            __builtin_memcpy(&x12, axr + 8 * hg, 16);
+            __builtin_memcpy(&x3, axr + 16, 16);
+            floatx16 R = {};
+            R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA, x12, R, 0, 0, 0);
+            R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA2, x3, R, 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) y[ts][r] = fmaf(R[r], ndv[r >> 2][r & 3], y[ts][r]);
-            }
+            for (int r = 0; r < 16; ++r) y[ts][r] = fmaf(R[r], ndv[r >> 2][r & 3], y[ts][r]);
         }
-        __syncthreads();
+    };
+
+    // Pipeline. Stage (sb, 0) lives in buffer 0, (sb, 1) in buffer 1; the loads of the next
+    // stage go to the buffer that the barrier just freed. The headers of super-block sb+1
+    // are loaded into registers while sb is computed.
+    uint32x4 hv = load_headers(0);
+    issue_stage(0, 0, s_aq0, s_bq0);
+    for (int sb = 0; sb < nsb; ++sb) {
+        // ---- first half: wait for (sb, 0) and the headers of sb, decode the headers
+        wait_vmem();
+        __syncthreads();                    // stage (sb,0) visible; (sb-1,1) and its min term done
+        if constexpr (!ISUMS) decode_headers(hv);
+        __syncthreads();                    // fold terms of sb visible
+        if (sb + 1 < nsb) hv = load_headers(sb + 1);
+        issue_stage(sb, 1, s_aq1, s_bq1);
+        compute_stage(sb, 0, s_aq0, s_bq0);
+
+        // ---- second half
+        wait_vmem();
+        __syncthreads();                    // stage (sb,1) visible; buffer 0 free
+        if (sb + 1 < nsb) issue_stage(sb + 1, 0, s_aq0, s_bq0);
+        compute_stage(sb, 1, s_aq1, s_bq1);
+        if constexpr (!ISUMS) min_term();
     }
 
     if constexpr (!ISUMS) {
@@ -288,7 +357,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
         const bool vec = ((N & 3) == 0) && ((((uintptr_t)Y) & 15) == 0);
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts) {
-            const int tok = m0 + tk[ts];
+            const int tok = m0 + 32 * ts + l32;
             if (tok >= M) continue;
             float* yrow = Y + (size_t)tok * N;
 #pragma unroll
