@@ -56,23 +56,26 @@ constexpr int TN = 128;           // weight rows per workgroup tile
 constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks
 constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
 
-// One LDS object per buffer, so the compiler can tell the stage being computed from the
-// one being loaded and does not make reads of the first wait for loads of the second.
-// Stage-buffer layouts, in 16-byte slots (a row pitch of 9 resp. 5 slots puts 16
-// consecutive tokens / rows of one ds_read_b128 phase on 16 distinct bank groups, and
-// every read address is one base register plus an immediate):
+// LDS of one group of four waves (one K range of the tile). Stage-buffer layouts, in
+// 16-byte slots (a row pitch of 9 resp. 5 slots puts 16 consecutive tokens / rows of one
+// ds_read_b128 phase on 16 distinct bank groups, and every read address is one base
+// register plus an immediate):
 //   q8 tile: token t, granule g (k 16g..16g+15 of the half) at slot 9t + g; slot 9t + 8 is pad
 //   raw qs:  row j, granule g (qs bytes 16g.. of the half)   at slot 5j + g; slot 5j + 4 is pad
 constexpr int AQ_SLOTS = TM * 9, BQ_SLOTS = TN * 5;          // 576 and 640: 9 and 10 slabs of 64
-__shared__ __attribute__((aligned(16))) uint8_t s_aq0[AQ_SLOTS * 16];
-__shared__ __attribute__((aligned(16))) uint8_t s_aq1[AQ_SLOTS * 16];
-__shared__ __attribute__((aligned(16))) uint8_t s_bq0[BQ_SLOTS * 16];
-__shared__ __attribute__((aligned(16))) uint8_t s_bq1[BQ_SLOTS * 16];
-__shared__ __attribute__((aligned(16))) float s_dsv[8][TN];           // d*sc per chunk, rows in C-register order per wave
-__shared__ __attribute__((aligned(16))) float2 s_ada[8][TM];          // (da, -1.5*2^23*da) per chunk and token
-__shared__ __attribute__((aligned(16))) uint16_t s_ax[TM * PC_STRIDE];  // bf16 pieces of da*ssum per token
-__shared__ __attribute__((aligned(16))) uint16_t s_bw[TN * 8];        // m per row and sub-block as bf16
-__shared__ __attribute__((aligned(16))) float s_bnd[TN];              // -dmin per row, rows in C-register order per wave
+struct GroupLds {
+    alignas(16) uint8_t aq0[AQ_SLOTS * 16];
+    alignas(16) uint8_t aq1[AQ_SLOTS * 16];
+    alignas(16) uint8_t bq0[BQ_SLOTS * 16];
+    alignas(16) uint8_t bq1[BQ_SLOTS * 16];
+    alignas(16) float dsv[8][TN];            // d*sc per chunk, rows in C-register order per wave
+    alignas(16) float2 ada[8][TM];           // (da, -1.5*2^23*da) per chunk and token
+    alignas(16) uint16_t ax[TM * PC_STRIDE]; // bf16 pieces of da*ssum per token
+    alignas(16) uint16_t bw[TN * 8];         // m per row and sub-block as bf16
+    alignas(16) float bnd[TN];               // -dmin per row, rows in C-register order per wave
+};
+static_assert(sizeof(GroupLds) == 52736, "LDS of one group");
+static_assert(4 * (AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= TM * TN * 4, "a group's stage buffers hold its partial tile");
 
 // Source offset of a pad slot: past every buffer's range, so the load writes zeros.
 constexpr unsigned PAD_OFF = 0x7F000000u;
@@ -111,22 +114,33 @@ __device__ __forceinline__ void split3_bf16(float v, uint16_t* dst, int stride)
 // complete: vmcnt(0), expcnt and lgkmcnt left at their maxima.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// One LDS-direct load: each lane's 16 bytes at voff go to LDS byte lds_wave_base + 16*lane.
+// Written as inline asm so that the compiler does not track it: its own wait insertion
+// can make unrelated LDS reads of the stage being computed wait for the prefetch.
+// Completion is waited for explicitly (wait_vmem) before the barrier that publishes the
+// stage. The LDS base must be wave-uniform.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, voff, 0, 0, 0);
+    const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
 }
 
-template <bool ISUMS>
-__global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
+// KS = number of four-wave groups per workgroup; group g computes the tile over its own
+// contiguous range of super-blocks and the partial sums are added in group order at the end.
+template <bool ISUMS, int KS>
+__global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qplane,
                                                          const uint32_t* __restrict__ hdr,
                                                          float* __restrict__ Y,
                                                          int32_t* __restrict__ S,
                                                          int M, int N, int K, int tiles_m, int total)
 {
+    __shared__ GroupLds lds_all[KS];
     int m_tile, n_tile;
     tile_coords(m_tile, n_tile, tiles_m, total);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
+    GroupLds& L = lds_all[grp];
+    const int tid = threadIdx.x & 255, lane = tid & 63;        // thread index inside the group
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = lane >> 5, l32 = lane & 31;
     const int m0 = m_tile * TM, n0 = n_tile * TN;
@@ -205,7 +219,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             const float dmin = half_bits_to_float(hv[0] >> 16);
             const uint32_t S0 = hv[1], S1 = hv[2], S2 = hv[3];
             const int pos = 32 * (j >> 5) + c_pos(j & 31);
-            s_bnd[pos] = -dmin;
+            L.bnd[pos] = -dmin;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 uint32_t sc, m;
@@ -217,8 +231,8 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                     sc = ((S2 >> s4) & 15u) | (((S0 >> s4) >> 6 & 3u) << 4);
                     m = ((S2 >> s4) >> 4 & 15u) | (((S1 >> s4) >> 6 & 3u) << 4);
                 }
-                s_dsv[s][pos] = d * (float)sc;                      // exact (17 bits)
-                s_bw[j * 8 + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
+                L.dsv[s][pos] = d * (float)sc;                      // exact (17 bits)
+                L.bw[j * 8 + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
             }
         } else {
             const int u = tid - TN, t = u >> 1, c4 = 4 * (u & 1);
@@ -227,8 +241,8 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                 const int c = c4 + e;
                 const uint32_t hw = hv[e];
                 const float da = half_bits_to_float(hw & 0xFFFFu);
-                s_ada[c][t] = make_float2(da, -MAGIC_F * da);       // exact
-                split3_bf16(da * (float)(int16_t)(hw >> 16), s_ax + t * PC_STRIDE + c, 8);   // da*ssum exact
+                L.ada[c][t] = make_float2(da, -MAGIC_F * da);       // exact
+                split3_bf16(da * (float)(int16_t)(hw >> 16), L.ax + t * PC_STRIDE + c, 8);   // da*ssum exact
             }
         }
     };
@@ -263,7 +277,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
             }
             if constexpr (!ISUMS) {
                 if (ts == 0) {
-                    const floatx4* dsvp = reinterpret_cast<const floatx4*>(&s_dsv[c][32 * wave + 16 * hg]);
+                    const floatx4* dsvp = reinterpret_cast<const floatx4*>(&L.dsv[c][32 * wave + 16 * hg]);
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) dsv[q4] = dsvp[q4];
                 }
@@ -281,7 +295,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
                         S[((size_t)tok * N + row) * nc + sb * 8 + c] = Fk[r] - MAGIC_BITS;
                 }
             } else {
-                const float2 dc = s_ada[c][32 * ts + l32];
+                const float2 dc = L.ada[c][32 * ts + l32];
                 const float da = dc.x, c0 = dc.y;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
@@ -303,7 +317,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
     // y += -dmin * R. MFMA 1 pairs x1 (k-group 0) and x2 (k-group 1) with m, MFMA 2 pairs x3
     // with m in k-group 0 only.
     auto min_term = [&]() {
-        const uint16_t* bwr = s_bw + wr * 8;            // m of this lane's weight row
+        const uint16_t* bwr = L.bw + wr * 8;            // m of this lane's weight row
         bf16x8 mA, mA2;
         __builtin_memcpy(&mA, bwr, 16);
         const int32x4 z4 = {0, 0, 0, 0};
@@ -311,12 +325,12 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
         const int32x4 mraw2 = hg ? z4 : mraw;
         __builtin_memcpy(&mA2, &mraw2, 16);
         floatx4 ndv[4];
-        const floatx4* ndp = reinterpret_cast<const floatx4*>(&s_bnd[32 * wave + 16 * hg]);
+        const floatx4* ndp = reinterpret_cast<const floatx4*>(&L.bnd[32 * wave + 16 * hg]);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) ndv[q4] = ndp[q4];
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts) {
-            const uint16_t* axr = s_ax + (32 * ts + l32) * PC_STRIDE;
+            const uint16_t* axr = L.ax + (32 * ts + l32) * PC_STRIDE;
             bf16x8 x12, x3;
             __builtin_memcpy(&x12, axr + 8 * hg, 16);
             __builtin_memcpy(&x3, axr + 16, 16);
@@ -331,24 +345,69 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 3) mmq_q4K_kernel(const uint8
     // Pipeline. Stage (sb, 0) lives in buffer 0, (sb, 1) in buffer 1; the loads of the next
     // stage go to the buffer that the barrier just freed. The headers of super-block sb+1
     // are loaded into registers while sb is computed.
-    uint32x4 hv = load_headers(0);
-    issue_stage(0, 0, s_aq0, s_bq0);
-    for (int sb = 0; sb < nsb; ++sb) {
+    // This group's super-blocks: [sb0, sb0 + cnt). Every group runs the same number of
+    // iterations (all waves of the workgroup meet at each barrier); a group with one
+    // super-block fewer idles through its last one.
+    const int nbase = nsb / KS, nrem = nsb % KS;
+    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
+    const int iters = nbase + (nrem ? 1 : 0);
+    uint32x4 hv;
+    if (cnt > 0) {
+        hv = load_headers(sb0);
+        issue_stage(sb0, 0, L.aq0, L.bq0);
+    }
+    for (int it = 0; it < iters; ++it) {
+        const bool act = it < cnt, more = it + 1 < cnt;
+        const int sb = sb0 + it;
         // ---- first half: wait for (sb, 0) and the headers of sb, decode the headers
         wait_vmem();
         __syncthreads();                    // stage (sb,0) visible; (sb-1,1) and its min term done
-        if constexpr (!ISUMS) decode_headers(hv);
+        if constexpr (!ISUMS)
+            if (act) decode_headers(hv);
         __syncthreads();                    // fold terms of sb visible
-        if (sb + 1 < nsb) hv = load_headers(sb + 1);
-        issue_stage(sb, 1, s_aq1, s_bq1);
-        compute_stage(sb, 0, s_aq0, s_bq0);
+        if (more) hv = load_headers(sb + 1);
+        if (act) {
+            issue_stage(sb, 1, L.aq1, L.bq1);
+            compute_stage(sb, 0, L.aq0, L.bq0);
+        }
 
         // ---- second half
         wait_vmem();
         __syncthreads();                    // stage (sb,1) visible; buffer 0 free
-        if (sb + 1 < nsb) issue_stage(sb + 1, 0, s_aq0, s_bq0);
-        compute_stage(sb, 1, s_aq1, s_bq1);
-        if constexpr (!ISUMS) min_term();
+        if (more) issue_stage(sb + 1, 0, L.aq0, L.bq0);
+        if (act) {
+            compute_stage(sb, 1, L.aq1, L.bq1);
+            if constexpr (!ISUMS) min_term();
+        }
+    }
+
+    if constexpr (!ISUMS && KS > 1) {
+        // Partial tiles of groups 1..KS-1 go through their own (now idle) stage buffers;
+        // group 0 adds them in group order. Layout: float4 q of sub-tile ts at
+        // ((4 ts + q) * 256 + thread) * 16 bytes, consecutive threads consecutive.
+        __syncthreads();                    // every group is done with its stage buffers
+        if (grp > 0) {
+            floatx4* red = reinterpret_cast<floatx4*>(L.aq0);
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[(4 * ts + q) * 256 + tid] = floatx4{y[ts][4 * q], y[ts][4 * q + 1], y[ts][4 * q + 2], y[ts][4 * q + 3]};
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KS; ++g2) {
+            const floatx4* red = reinterpret_cast<const floatx4*>(lds_all[g2].aq0);
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx4 p = red[(4 * ts + q) * 256 + tid];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[ts][4 * q + e] += p[e];
+                }
+        }
     }
 
     if constexpr (!ISUMS) {
@@ -388,11 +447,24 @@ hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* 
     const int total = tiles_m * tiles_n;
     const int8_t* qplane = static_cast<const int8_t*>(xq);
     const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
-    if (isums)
-        hipLaunchKernelGGL(mmq_q4K_kernel<true>, dim3(total), dim3(256), 0, s, static_cast<const uint8_t*>(w),
-                           qplane, hdr, y, isums, (int)M, (int)N, (int)K, tiles_m, total);
-    else
-        hipLaunchKernelGGL(mmq_q4K_kernel<false>, dim3(total), dim3(256), 0, s, static_cast<const uint8_t*>(w),
-                           qplane, hdr, y, isums, (int)M, (int)N, (int)K, tiles_m, total);
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    // At most one tile per CU (256 CUs): split each tile's super-blocks over three
+    // four-wave groups, so each SIMD still holds three waves.
+    const bool split = total <= 256 && K / 256 >= 3;
+    if (isums) {
+        if (split)
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+        else
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+    } else {
+        if (split)
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+        else
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+    }
     return hipGetLastError();
 }
