@@ -7,9 +7,9 @@
 // q6_K kernel of "r40 - __launch_bounds__(256,3) third resident block" (sec. 5).
 //
 // MI355X design:
-//  * Tile 64 tokens x 128 weight rows, 4 waves; wave w = weight rows 32w..32w+31 (MFMA row
-//    side) x 64 tokens (two 32x32 sub-tiles on the column side): da is one value per lane,
-//    d*sc is read once per sub-block for both token sub-tiles.
+//  * Tile 64 tokens x 128 weight rows per group of 4 waves; wave w = weight rows
+//    32w..32w+31 (MFMA row side) x 64 tokens (two 32x32 sub-tiles on the column side):
+//    da is one value per lane, d*sc is read once per sub-block for both token sub-tiles.
 //  * Integer stage: v_mfma_i32_32x32x16_i8 per (token sub-tile, 16-wide sub-block). The
 //    weight operand v = q6 - 32 is assembled per byte in registers from the raw ql / qh bytes
 //    in LDS: q6 = low4 | high2 << 4, and v = ((q6 | 0x80) - 0x20) ^ 0x80 turns the unsigned
@@ -17,12 +17,20 @@
 //  * The MFMA accumulates onto the bits of 1.5*2^23, so its int32 result read as f32 is
 //    1.5*2^23 + J exactly (|J| <= 32*127*16 < 2^22): e = fma(F, da, -1.5*2^23*da) is
 //    round(da*J) and y = fma(e, d*sc, y). Two VALU ops per output and sub-block.
-//  * q6_K rows start only 2-byte aligned (210-byte blocks): staging reads aligned dwords and
-//    shifts them into place with v_alignbyte, never a misaligned wide load.
-//  * LDS: inside every 32-byte group of q, ql and qh the 8-byte pieces 1 and 2 are swapped at
-//    staging, so one 16-byte read gives a lane its 8 bytes of both sub-blocks of a chunk
-//    (k-group l>>5 of each K=16 MFMA). Rows are XOR-swizzled in 16-byte granules so reads of
-//    16 consecutive rows hit 16 distinct bank groups.
+//  * Staging is a two-deep pipeline of half super-blocks (128 k, one barrier per stage).
+//    The q8 tile of stage h+1 comes by dword LDS-direct loads (buffer_load_dword ... lds)
+//    issued before stage h is computed. The weight bytes of stage h+1 (rows start only
+//    2-byte aligned: 210-byte blocks) are fetched into registers as aligned dwords at the
+//    same time, shifted into place with v_alignbyte and written to the other LDS buffer
+//    after stage h's compute, together with d*sc; the q8_1 header words come by dword
+//    LDS-direct loads with the q8 tile.
+//  * LDS: inside every 32-byte group of q, ql and qh the 8-byte pieces 1 and 2 are swapped
+//    (the dword loads pick their source accordingly), so one 16-byte read gives a lane its
+//    8 bytes of both sub-blocks of a chunk (k-group l>>5 of each K=16 MFMA). Rows are
+//    XOR-swizzled in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups.
+//  * When the matrix has at most one tile per CU, three groups of four waves share a
+//    workgroup, each over a contiguous range of super-blocks, and the partial tiles are
+//    added in group order through LDS at the end (three waves per SIMD, deterministic).
 #include "qpg_common.h"
 
 namespace qpg {
@@ -30,18 +38,33 @@ namespace q6k {
 
 typedef unsigned uint32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TM = 64;
 constexpr int TN = 128;
-constexpr int DA_STRIDE = 20;     // floats per token: per chunk pair p: da_2p, da_2p+1, c0_2p, c0_2p+1 (+pad)
+constexpr int HALF = 128;          // k per pipeline stage
 
-struct alignas(16) Smem {
-    alignas(16) uint8_t aq[TM * 256];          // q8 tile, permuted pieces, granule g of token t at g ^ (t & 15)
-    alignas(16) uint8_t bl[TN * 128];          // ql, permuted pieces, granule g of row j at g ^ ((j >> 1) & 7)
-    alignas(16) uint8_t bh[TN * 64];           // qh, permuted pieces, granule g of row j at g ^ ((j >> 2) & 3)
-    alignas(16) float bdsc[16][TN];            // d*sc per sub-block, rows in C-register order per wave
-    alignas(16) float ada[TM * DA_STRIDE];     // da and -1.5*2^23*da per token and chunk
+// One pipeline stage (half a super-block) of one group.
+//   aq:  token t at 128 t; granule G (chunk G>>1, k-group G&1, pieces swapped) at slot G ^ ((t >> 1) & 7)
+//   bl:  ql half, row j at 64 j; granule G (group G>>1, part G&1) at slot G ^ ((j >> 2) & 3)
+//   bh:  qh half, row j at 32 j; granule G at slot G ^ ((j >> 3) & 1)
+struct StageLds {
+    alignas(16) uint8_t aq[TM * HALF];
+    alignas(16) uint8_t bl[TN * 64];
+    alignas(16) uint8_t bh[TN * 32];
+    alignas(16) float dsc[8][TN];       // d*sc per sub-block of the stage, rows in C-register order per wave
+    alignas(16) uint32_t hw[4][TM];     // q8_1 header words (fp16 da | ssum) per chunk of the stage and token
+    alignas(16) uint32_t spare[256];    // keeps a group at 52 KiB (three per CU)
 };
+struct GroupLds {
+    StageLds st[2];
+};
+static_assert(sizeof(GroupLds) == 53248, "LDS of one group");
+static_assert(sizeof(GroupLds) >= TM * TN * 4, "a group's buffers hold its partial tile");
+
+__device__ __forceinline__ int aq_sw(int t) { return (t >> 1) & 7; }
+__device__ __forceinline__ int bl_sw(int j) { return (j >> 2) & 3; }
+__device__ __forceinline__ int bh_sw(int j) { return (j >> 3) & 1; }
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
 {
@@ -57,65 +80,97 @@ __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_
 
 __device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
 
-__device__ __forceinline__ uint32_t ld32(const uint8_t* p)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// One dword LDS-direct load: each lane's 4 bytes at voff go to LDS byte lds_wave_base + 4*lane.
+// Inline asm, so that the compiler's own waits do not tie unrelated LDS reads to it;
+// completion is waited for explicitly (wait_vmem) before the barrier that publishes it.
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
-    return *reinterpret_cast<const uint32_t*>(p);     // p is 4-byte aligned
+    const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
 }
 
-// 16 bytes starting at the 2-byte aligned address p, read as aligned dwords from
-// [p - sh, p - sh + 16 + 4*(sh != 0)), sh = p & 2.
-__device__ __forceinline__ uint32x4 ld16_a2(const uint8_t* p, uint32_t sh)
-{
-    const uint8_t* a = p - sh;
-    uint32x4 v;
-    const uint32_t w0 = ld32(a), w1 = ld32(a + 4), w2 = ld32(a + 8), w3 = ld32(a + 12);
-    if (sh) {
-        const uint32_t w4 = ld32(a + 16);
-        v[0] = __builtin_amdgcn_alignbyte(w1, w0, 2);
-        v[1] = __builtin_amdgcn_alignbyte(w2, w1, 2);
-        v[2] = __builtin_amdgcn_alignbyte(w3, w2, 2);
-        v[3] = __builtin_amdgcn_alignbyte(w4, w3, 2);
-    } else {
-        v[0] = w0; v[1] = w1; v[2] = w2; v[3] = w3;
-    }
-    return v;
-}
+// Source byte, inside a 32-byte chunk, of dword w4 of granule G's half x = G & 1: the
+// granule holds pieces x and 2 + x (8 bytes each) of the chunk.
+__device__ __forceinline__ int perm_src(int G, int w4) { return 8 * ((w4 < 2 ? 0 : 2) + (G & 1)) + 4 * (w4 & 1); }
 
-// A 16-byte granule at byte 16*gi (gi = 0/1) of a 32-byte group, stored with the group's
-// pieces 1 and 2 swapped: bytes 0-7 go to piece gi, bytes 8-15 to piece 2 + gi. `grp` is the
-// group's LDS base; the pieces land in granules (2*G + 0/1) ^ sw of the row.
-__device__ __forceinline__ void st_perm(uint8_t* row, int G, int gi, int sw, uint32x4 v)
+template <bool ISUMS, int KS>
+__global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
+    float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total)
 {
-    const uint32x2 lo = {v[0], v[1]}, hi = {v[2], v[3]};
-    // piece P (0..3) of group G sits in granule 2G + (P >> 1), half (P & 1)
-    *reinterpret_cast<uint32x2*>(row + 16 * ((2 * G + 0) ^ sw) + 8 * gi) = lo;   // piece gi
-    *reinterpret_cast<uint32x2*>(row + 16 * ((2 * G + 1) ^ sw) + 8 * gi) = hi;   // piece 2 + gi
-}
-
-template <bool ISUMS>
-__global__ void __launch_bounds__(256, ISUMS ? 1 : 2) mmq_q6K_kernel(const uint8_t* __restrict__ W,
-                                                                     const int8_t* __restrict__ qplane,
-                                                                     const uint32_t* __restrict__ hdr,
-                                                                     float* __restrict__ Y,
-                                                                     int32_t* __restrict__ S,
-                                                                     int M, int N, int K, int tiles_m, int total)
-{
-    __shared__ Smem sm;
+    __shared__ GroupLds lds_all[KS];
     int m_tile, n_tile;
     tile_coords(m_tile, n_tile, tiles_m, total);
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
+    GroupLds& G = lds_all[grp];
+    const int tid = threadIdx.x & 255, lane = tid & 63;        // thread index inside the group
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = lane >> 5, l32 = lane & 31;
     const int m0 = m_tile * TM, n0 = n_tile * TN;
     const int nsb = K / QK_K, nc = K / QK8, nu = K / 16;
-    const size_t wrow = (size_t)nsb * Q6K_BYTES;
+    const int wrow = nsb * Q6K_BYTES;
 
-    const int rows_t = min(TM, M - m0);
+    // Buffer descriptors over this tile's rows: loads past the last token / weight row
+    // return zeros.
+    const int rows_w = min(TN, N - n0), rows_t = min(TM, M - m0);
+    const __amdgpu_buffer_rsrc_t rW =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * wrow), 0, rows_w * wrow, 0x00020000);
     const __amdgpu_buffer_rsrc_t rQ =
         __builtin_amdgcn_make_buffer_rsrc((void*)(qplane + (size_t)m0 * K), 0, rows_t * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rH =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
+    // ---- q8 tile: 32 dword LDS-direct loads per stage, 8 per wave. Load m of wave w
+    // covers LDS dwords 64(w + 4m) ..: tokens t = 2(w + 4m) + (lane >> 5), dword lane & 31
+    // of the row. The swizzle of token t is (w + 4m) & 7, so two per-lane patterns suffice.
+    int voQ[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int sw = (wave + 4 * par) & 7, wd = lane & 31;
+        const int Gq = (wd >> 2) ^ sw, w4 = wd & 3;
+        voQ[par] = (2 * wave + (lane >> 5)) * K + 32 * (Gq >> 1) + perm_src(Gq, w4);
+    }
+    // q8_1 header words of the stage: wave w brings chunk w of the stage, lane = token.
+    const int voH = lane * nc * 4 + 4 * wave;
+    auto issue_q8 = [&](int sb, int hh, StageLds& st) {
+        const int off = sb * QK_K + hh * HALF;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            lds_load4(rQ, st.aq + 256 * (wave + 4 * m), voQ[m & 1] + 8 * m * K + off);
+        if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
+    };
+
+    // ---- weights of one stage into registers. Task A (all threads): ql group tid >> 7
+    // (32 bytes) of row tid & 127; task B (threads < 128): the qh half (32 bytes) of row
+    // tid, sc[8hh..8hh+7] and d. Each 32-byte group is 9 aligned dwords from
+    // (block + offset - sh), sh = block offset & 2.
+    struct Pre {
+        uint32_t a[9], b[9], sc[3], dh;
+    };
+    auto load_stage = [&](int sb, int hh, Pre& p) {
+        const int jA = tid & 127, grpA = tid >> 7;
+        const int oA = jA * wrow + sb * Q6K_BYTES;
+        const int shA = oA & 2;
+        const int srcA = oA + 64 * hh + 32 * grpA - shA;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) p.a[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcA + 4 * i, 0, 0);
+        if (tid < TN) {
+            const int srcB = oA + 128 + 32 * hh - shA;
+#pragma unroll
+            for (int i = 0; i < 9; ++i) p.b[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcB + 4 * i, 0, 0);
+            if constexpr (!ISUMS) {
+                // sc[8hh..8hh+7] at oA + 192 + 8hh: 2 aligned dwords, a third when shifted (the
+                // third never passes the block end: it ends at oA + 202 + 8hh)
+                const int srcS = oA + 192 + 8 * hh - shA;
+                p.sc[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS, 0, 0);
+                p.sc[1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS + 4, 0, 0);
+                p.sc[2] = shA ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS + 8, 0, 0) : 0u;
+                p.dh = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rW, oA + 208, 0, 0);
+            }
+        }
+    };
     int32x16 magic;
 #pragma unroll
     for (int r = 0; r < 16; ++r) magic[r] = MAGIC_BITS;
@@ -126,129 +181,158 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 2) mmq_q6K_kernel(const uint8
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
     const int wr = 32 * wave + l32;                  // weight row of this lane's A operand
-    int tk[2];
-#pragma unroll
-    for (int ts = 0; ts < 2; ++ts) tk[ts] = 32 * ts + l32;
+    const int tsw = aq_sw(l32);                      // tokens l32 and l32 + 32 share the swizzle
 
-    for (int sb = 0; sb < nsb; ++sb) {
-        // ---------------- stage A: q8 tile; 16-byte granule p of a row is sub-block p
+    // Write a stage's prefetched weight bytes and d*sc into LDS.
+    auto commit = [&](const Pre& p, int sb, StageLds& st) {
+        const int jA = tid & 127, grpA = tid >> 7;
+        const int shA = (jA * wrow + sb * Q6K_BYTES) & 2;
+        uint32_t ga[8];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int g = it * 256 + tid, t = g >> 4, part = g & 15;
-            const uint32x4 v = __builtin_bit_cast(
-                uint32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, t * K + sb * QK_K + part * 16, 0, 0));
-            st_perm(sm.aq + t * 256, part >> 1, part & 1, t & 15, v);
-        }
+        for (int i = 0; i < 8; ++i) ga[i] = __builtin_amdgcn_alignbyte(p.a[i + 1], p.a[i], shA);
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int h = it * 256 + tid, t = h >> 3, c = h & 7;
-            const uint32_t hw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rH, (t * nc + sb * 8 + c) * 4, 0, 0);
-            const float da = half_bits_to_float(hw & 0xFFFFu);
-            float* ad = sm.ada + t * DA_STRIDE + 4 * (c >> 1) + (c & 1);
-            ad[0] = da;
-            ad[2] = -MAGIC_F * da;                                                  // exact
+        for (int x = 0; x < 2; ++x) {
+            const int Gl = 2 * grpA + x;
+            const uint32x4 v = {ga[2 * x], ga[2 * x + 1], ga[4 + 2 * x], ga[5 + 2 * x]};
+            *reinterpret_cast<uint32x4*>(st.bl + 64 * jA + 16 * (Gl ^ bl_sw(jA))) = v;
         }
-        // ---------------- stage B: ql (8 granules) and qh (4 granules) per row
-#pragma unroll
-        for (int it = 0; it < 6; ++it) {
-            const int g = it * 256 + tid, j = g / 12, gi = g - 12 * j;
-            uint32x4 v = {0u, 0u, 0u, 0u};
-            if (n0 + j < N) {
-                const size_t off = (size_t)(n0 + j) * wrow + (size_t)sb * Q6K_BYTES;
-                v = ld16_a2(W + off + 16 * gi, (uint32_t)(off & 2));
-            }
-            if (gi < 8)
-                st_perm(sm.bl + j * 128, gi >> 1, gi & 1, (j >> 1) & 7, v);
-            else
-                st_perm(sm.bh + j * 64, (gi - 8) >> 1, gi & 1, (j >> 2) & 3, v);
-        }
-        // ---------------- stage B: d * sc[u] per row, in C-register order
         if (tid < TN) {
-            const int j = tid;
-            const int pos = 32 * (j >> 5) + c_pos(j & 31);
-            if (n0 + j < N) {
-                const size_t off = (size_t)(n0 + j) * wrow + (size_t)sb * Q6K_BYTES;
-                const uint32x4 scw = ld16_a2(W + off + 192, (uint32_t)(off & 2));
-                const float d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(W + off + 208));
+            uint32_t gb[8];
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    sm.bdsc[u][pos] = d * (float)(int)(int8_t)(scw[u >> 2] >> (8 * (u & 3)));   // exact
-            } else {
+            for (int i = 0; i < 8; ++i) gb[i] = __builtin_amdgcn_alignbyte(p.b[i + 1], p.b[i], shA);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) sm.bdsc[u][pos] = 0.0f;
+            for (int x = 0; x < 2; ++x) {
+                const uint32x4 v = {gb[2 * x], gb[2 * x + 1], gb[4 + 2 * x], gb[5 + 2 * x]};
+                *reinterpret_cast<uint32x4*>(st.bh + 32 * jA + 16 * (x ^ bh_sw(jA))) = v;
+            }
+            if constexpr (!ISUMS) {
+                const uint32_t s0 = __builtin_amdgcn_alignbyte(p.sc[1], p.sc[0], shA);
+                const uint32_t s1 = __builtin_amdgcn_alignbyte(p.sc[2], p.sc[1], shA);
+                const float d = half_bits_to_float(p.dh & 0xFFFFu);
+                const int pos = 32 * (jA >> 5) + c_pos(jA & 31);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const uint32_t w = u < 4 ? s0 : s1;
+                    st.dsc[u][pos] = d * (float)(int)(int8_t)(w >> (8 * (u & 3)));      // exact
+                }
             }
         }
-        __syncthreads();
+    };
 
-        // ---------------- integer stage + fold
+    // Integer stage + fold over the four chunks of one stage (chunk cl = sub-blocks 2cl and
+    // 2cl+1 of the stage = sub-blocks 8hh + 2cl, +1 of the super-block).
+    auto compute_stage = [&](int sb, int hh, const StageLds& st) {
+        const uint32x4 qh = *reinterpret_cast<const uint32x4*>(st.bh + 32 * wr + 16 * (hg ^ bh_sw(wr)));
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-            // keep each chunk's loads and products together: bounds the live registers to one
-            // chunk's operands. (Two resident workgroups per CU: at three the 168-register budget
-            // spills, and the spilling form measured 1.6x slower.)
+        for (int cl = 0; cl < 4; ++cl) {
             __builtin_amdgcn_sched_barrier(0);
-            const int h = cc >> 2, g = cc & 3;
-            // weight operand for both sub-blocks of the chunk: 16 bytes of ql and of qh
-            const uint32x4 ql = *reinterpret_cast<const uint32x4*>(
-                sm.bl + wr * 128 + 16 * ((4 * h + 2 * (g & 1) + hg) ^ ((wr >> 1) & 7)));
-            const uint32x4 qh = *reinterpret_cast<const uint32x4*>(
-                sm.bh + wr * 64 + 16 * ((2 * h + hg) ^ ((wr >> 2) & 3)));
+            const uint32x4 ql = *reinterpret_cast<const uint32x4*>(st.bl + 64 * wr + 16 * ((2 * (cl & 1) + hg) ^ bl_sw(wr)));
             uint32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = (ql[e] >> (4 * (g >> 1))) & 0x0F0F0F0Fu;
-                const uint32_t hi = ((qh[e] >> (2 * g)) & 0x03030303u) << 4;
-                const uint32_t q6 = lo | hi | 0x80808080u;                  // bit 7 set: no borrow below
-                v[e] = (q6 - 0x20202020u) ^ 0x80808080u;                    // signed q6 - 32 per byte
+                const uint32_t lo = (ql[e] >> (4 * (cl >> 1))) & 0x0F0F0F0Fu;
+                const uint32_t hi = ((qh[e] >> (2 * cl)) & 0x03030303u) << 4;
+                v[e] = ((lo | hi | 0x80808080u) - 0x20202020u) ^ 0x80808080u;   // signed q6 - 32 per byte
             }
-            const long a0 = (long)(((unsigned long)v[1] << 32) | v[0]);    // sub-block 2cc, k-group hg
-            const long a1 = (long)(((unsigned long)v[3] << 32) | v[2]);    // sub-block 2cc+1
-            floatx4 s0[4], s1[4];
-            if constexpr (!ISUMS) {
-                const floatx4* p0 = reinterpret_cast<const floatx4*>(&sm.bdsc[2 * cc][32 * wave + 16 * hg]);
-                const floatx4* p1 = reinterpret_cast<const floatx4*>(&sm.bdsc[2 * cc + 1][32 * wave + 16 * hg]);
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    s0[q4] = p0[q4];
-                    s1[q4] = p1[q4];
-                }
-            }
+            const long a0 = (long)(((unsigned long)v[1] << 32) | v[0]);      // sub-block 2cl, k-group hg
+            const long a1 = (long)(((unsigned long)v[3] << 32) | v[2]);      // sub-block 2cl+1
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
-                const uint32x4 bq = *reinterpret_cast<const uint32x4*>(
-                    sm.aq + tk[ts] * 256 + 16 * ((2 * cc + hg) ^ (tk[ts] & 15)));
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32x4 bq = *reinterpret_cast<const uint32x4*>(st.aq + 128 * (32 * ts + l32) +
+                                                                        16 * ((2 * cl + hg) ^ tsw));
                 const long b0 = (long)(((unsigned long)bq[1] << 32) | bq[0]);
                 const long b1 = (long)(((unsigned long)bq[3] << 32) | bq[2]);
                 const int32x16 F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, magic, 0, 0, 0);
                 const int32x16 F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, b1, magic, 0, 0, 0);
                 if constexpr (ISUMS) {
-                    const int tok = m0 + tk[ts];
+                    const int tok = m0 + 32 * ts + l32;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = n0 + 32 * wave + c_row(r, lane);
                         if (tok < M && row < N) {
-                            int32_t* dst = S + ((size_t)tok * N + row) * nu + sb * 16 + 2 * cc;
+                            int32_t* dst = S + ((size_t)tok * N + row) * nu + sb * 16 + 8 * hh + 2 * cl;
                             dst[0] = F0[r] - MAGIC_BITS;
                             dst[1] = F1[r] - MAGIC_BITS;
                         }
                     }
                 } else {
-                    const floatx4 dc = *reinterpret_cast<const floatx4*>(sm.ada + tk[ts] * DA_STRIDE + 4 * (cc >> 1));
-                    const float da = dc[cc & 1], c0 = dc[2 + (cc & 1)];
+                    const float da = half_bits_to_float(st.hw[cl][32 * ts + l32] & 0xFFFFu);
+                    const float c0 = -MAGIC_F * da;                                       // exact
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4)
+                    for (int s = 0; s < 2; ++s) {
+                        const int32x16 Fs = s ? F1 : F0;
+                        const floatx4* dp = reinterpret_cast<const floatx4*>(&st.dsc[2 * cl + s][32 * wave + 16 * hg]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int r = 4 * q4 + e;
-                            const float e0 = fmaf(__int_as_float(F0[r]), da, c0);    // round(da * J0)
-                            const float e1 = fmaf(__int_as_float(F1[r]), da, c0);    // round(da * J1)
-                            y[ts][r] = fmaf(e0, s0[q4][e], y[ts][r]);
-                            y[ts][r] = fmaf(e1, s1[q4][e], y[ts][r]);
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const floatx4 d4 = dp[q4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const int r = 4 * q4 + e;
+                                const float ev = fmaf(__int_as_float(Fs[r]), da, c0);    // round(da * J)
+                                y[ts][r] = fmaf(ev, d4[e], y[ts][r]);
+                            }
                         }
+                    }
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // folds of this stage done here (not sunk past the next barrier)
+        asm volatile("" : "+v"(y[0]), "+v"(y[1]));
+    };
+
+    // Pipeline over this group's stages: super-blocks [sb0, sb0 + cnt), two stages each.
+    // Every group runs the same number of stages so that all waves meet at every barrier.
+    const int nbase = nsb / KS, nrem = nsb % KS;
+    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
+    const int nst = 2 * cnt, nst_all = 2 * (nbase + (nrem ? 1 : 0));
+    Pre pre;
+    if (nst > 0) {
+        issue_q8(sb0, 0, G.st[0]);
+        load_stage(sb0, 0, pre);
+        commit(pre, sb0, G.st[0]);
+    }
+    for (int h = 0; h < nst_all; ++h) {
+        const int sb = sb0 + (h >> 1), hh = h & 1, cur = h & 1;
+        wait_vmem();
+        __syncthreads();                    // stage h visible in buffer cur; buffer cur^1 free
+        const bool next = h + 1 < nst;
+        const int sbn = sb0 + ((h + 1) >> 1), hhn = (h + 1) & 1;
+        if (next) {
+            issue_q8(sbn, hhn, G.st[cur ^ 1]);
+            load_stage(sbn, hhn, pre);
+        }
+        if (h < nst) compute_stage(sb, hh, G.st[cur]);
+        if (next) commit(pre, sbn, G.st[cur ^ 1]);
+    }
+
+    if constexpr (!ISUMS && KS > 1) {
+        // Partial tiles of groups 1..KS-1 through their own (now idle) LDS; group 0 adds
+        // them in group order. float4 q of sub-tile ts at ((4 ts + q) * 256 + thread) * 16.
         __syncthreads();
+        if (grp > 0) {
+            floatx4* red = reinterpret_cast<floatx4*>(&G);
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[(4 * ts + q) * 256 + tid] = floatx4{y[ts][4 * q], y[ts][4 * q + 1], y[ts][4 * q + 2], y[ts][4 * q + 3]};
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll
+        for (int g2 = 1; g2 < KS; ++g2) {
+            const floatx4* red = reinterpret_cast<const floatx4*>(&lds_all[g2]);
+#pragma unroll
+            for (int ts = 0; ts < 2; ++ts)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const floatx4 p = red[(4 * ts + q) * 256 + tid];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) y[ts][4 * q + e] += p[e];
+                }
+        }
     }
 
     if constexpr (!ISUMS) {
@@ -257,7 +341,7 @@ __global__ void __launch_bounds__(256, ISUMS ? 1 : 2) mmq_q6K_kernel(const uint8
         const bool vec = ((N & 3) == 0) && ((((uintptr_t)Y) & 15) == 0);
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts) {
-            const int tok = m0 + tk[ts];
+            const int tok = m0 + 32 * ts + l32;
             if (tok >= M) continue;
             float* yrow = Y + (size_t)tok * N;
 #pragma unroll
@@ -288,11 +372,23 @@ hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* 
     const int total = tiles_m * tiles_n;
     const int8_t* qplane = static_cast<const int8_t*>(xq);
     const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
-    if (isums)
-        hipLaunchKernelGGL(mmq_q6K_kernel<true>, dim3(total), dim3(256), 0, s, static_cast<const uint8_t*>(w),
-                           qplane, hdr, y, isums, (int)M, (int)N, (int)K, tiles_m, total);
-    else
-        hipLaunchKernelGGL(mmq_q6K_kernel<false>, dim3(total), dim3(256), 0, s, static_cast<const uint8_t*>(w),
-                           qplane, hdr, y, isums, (int)M, (int)N, (int)K, tiles_m, total);
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    // At most one tile per CU (256 CUs): split each tile's super-blocks over three groups.
+    const bool split = total <= 256 && K / 256 >= 3;
+    if (isums) {
+        if (split)
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+        else
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+    } else {
+        if (split)
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+        else
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total);
+    }
     return hipGetLastError();
 }
