@@ -12,8 +12,8 @@
 //    da is one value per lane, d*sc is read once per sub-block for both token sub-tiles.
 //  * Integer stage: v_mfma_i32_32x32x16_i8 per (token sub-tile, 16-wide sub-block). The
 //    weight operand v = q6 - 32 is assembled per byte in registers from the raw ql / qh bytes
-//    in LDS: q6 = low4 | high2 << 4, and v = ((q6 | 0x80) - 0x20) ^ 0x80 turns the unsigned
-//    6-bit value into the signed int8 q6 - 32 without any borrow between bytes.
+//    in LDS: q6 = low4 + (high2 << 4), and v = (q6 + 0x60) ^ 0x80 turns the unsigned 6-bit
+//    value into the signed int8 q6 - 32 with no carry between bytes (q6 + 96 <= 159).
 //  * The MFMA accumulates onto the bits of 1.5*2^23, so its int32 result read as f32 is
 //    1.5*2^23 + J exactly (|J| <= 32*127*16 < 2^22): e = fma(F, da, -1.5*2^23*da) is
 //    round(da*J) and y = fma(e, d*sc, y). Two VALU ops per output and sub-block.
@@ -231,8 +231,12 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t lo = (ql[e] >> (4 * (cl >> 1))) & 0x0F0F0F0Fu;
-                const uint32_t hi = ((qh[e] >> (2 * cl)) & 0x03030303u) << 4;
-                v[e] = ((lo | hi | 0x80808080u) - 0x20202020u) ^ 0x80808080u;   // signed q6 - 32 per byte
+                // bits 2cl, 2cl+1 of each qh byte moved to bits 4, 5
+                const uint32_t hs = cl < 2 ? qh[e] << (4 - 2 * cl) : qh[e] >> (2 * cl - 4);
+                const uint32_t hi = hs & 0x30303030u;
+                // q6 = lo + hi <= 63 per byte; q6 + 96 <= 159 never carries into the next byte,
+                // and (q6 + 96) ^ 0x80 is the signed byte q6 - 32
+                v[e] = (lo + hi + 0x60606060u) ^ 0x80808080u;
             }
             const long a0 = (long)(((unsigned long)v[1] << 32) | v[0]);      // sub-block 2cl, k-group hg
             const long a1 = (long)(((unsigned long)v[3] << 32) | v[2]);      // sub-block 2cl+1
