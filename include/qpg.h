@@ -118,6 +118,27 @@ int mmq_q4K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t 
 int mmq_q6K_isums(const void* w, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
                   qpg_stream_t stream);
 
+/*
+ * Prepared q6_K weights (the q6_K "prepare" pass of "r41"-"r53" in the pages' NEXT
+ * list: a one-time repack into an aligned layout that the kernel stages with plain 16-byte
+ * direct-to-LDS copies). q6K_prepare reads raw q6_K blocks w [N][K/256] (4-byte aligned)
+ * and writes wp (qpg_q6K_prep_bytes(N, K) bytes, 16-byte aligned, caller-owned): per
+ * 128-row tile and super-block two 16 KiB stage images holding the ql / qh bytes
+ * (reordered and swizzled) and d*sc[u] as f32 (exact). The layout is library-internal:
+ * wp is only meaningful to the _prep entry points of the same library, and must be
+ * prepared again after w changes. Rows past N are zero-filled.
+ * mmq_q6K_prep_q8 / mmq_q6K_prep_isums compute exactly what mmq_q6K_q8 / mmq_q6K_isums
+ * compute from the raw blocks (the integer sums are identical; outputs agree to the
+ * same tolerance). qpg_q6K_prep_bytes returns 0 for an unsupported shape
+ * (N < 1, K % 256 != 0, K > 2^24 - 256).
+ */
+size_t qpg_q6K_prep_bytes(int64_t N, int64_t K);
+int q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, qpg_stream_t stream);
+int mmq_q6K_prep_q8(const void* wp, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                    qpg_stream_t stream);
+int mmq_q6K_prep_isums(const void* wp, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                       qpg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,8 @@ load the library; the first call does, and fails loudly if it has not been built
 from . import inputs  # noqa: F401  (seeded synthetic inputs; no compute)
 
 __all__ = ["inputs", "q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8", "mmq_q6K_q8",
-           "mmq_q4K_isums", "mmq_q6K_isums", "QPGError"]
+           "mmq_q4K_isums", "mmq_q6K_isums", "q6K_prep_bytes", "q6K_prepare", "mmq_q6K_prep_q8",
+           "mmq_q6K_prep_isums", "QPGError"]
 
 
 def __getattr__(name):

@@ -77,9 +77,61 @@ int mmq_checked(bool q6, const void* w, const void* xq, float* y, int32_t* s, in
                         : qpg_launch_mmq_q4K(w, xq, y, s, M, N, K, st));
 }
 
+// Prepared q6_K: the per-tile record offsets (nsb * 32 KiB) must stay below 2^31.
+constexpr int64_t kPrepTile = 128, kPrepSb = 32768;
+
+int prep_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N < kMaxDim && K >= 256 && K % 256 == 0 && K <= kMaxK && (K / 256) * kPrepSb < kMaxDim &&
+           ((N + kPrepTile - 1) / kPrepTile) * (K / 256) < kMaxDim;
+}
+
+int mmq_prep_checked(const void* wp, const void* xq, float* y, int32_t* s, int64_t M, int64_t N, int64_t K,
+                     hipStream_t st)
+{
+    if (!wp || !xq || (!y && !s)) return QPG_EINVAL;
+    int rc = check_mmq_shape(M, N, K);
+    if (rc != QPG_OK) return rc;
+    if (!prep_shape_ok(N, K)) return QPG_EINVAL;
+    if (s && M * N * (K / 16) >= ((int64_t)1 << 40)) return QPG_EINVAL;
+    if (!aligned(wp, 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4))) return QPG_EALIGN;
+    rc = check_device();
+    if (rc != QPG_OK) return rc;
+    return status_of(qpg_launch_mmq_q6K_prep(wp, xq, y, s, M, N, K, st));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t qpg_q6K_prep_bytes(int64_t N, int64_t K)
+{
+    if (!prep_shape_ok(N, K)) return 0;
+    return (size_t)(((N + kPrepTile - 1) / kPrepTile) * (K / 256) * kPrepSb);
+}
+
+int q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!w || !wp) return QPG_EINVAL;
+    if (!prep_shape_ok(N, K)) return QPG_EINVAL;
+    if (!aligned(w, 4) || !aligned(wp, 16)) return QPG_EALIGN;
+    const int rc = check_device();
+    if (rc != QPG_OK) return rc;
+    return status_of(qpg_launch_q6K_prepare(w, wp, N, K, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mmq_q6K_prep_q8(const void* wp, const void* xq, float* y, int64_t M, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!y) return QPG_EINVAL;
+    return mmq_prep_checked(wp, xq, y, nullptr, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_prep_isums(const void* wp, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                       qpg_stream_t stream)
+{
+    if (!s) return QPG_EINVAL;
+    return mmq_prep_checked(wp, xq, nullptr, s, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
 
 const char* qpg_strerror(int status)
 {

@@ -31,6 +31,8 @@
 //  * When the matrix has at most one tile per CU, three groups of four waves share a
 //    workgroup, each over a contiguous range of super-blocks, and the partial tiles are
 //    added in group order through LDS at the end (three waves per SIMD, deterministic).
+#include <cstddef>
+
 #include "qpg_common.h"
 
 namespace qpg {
@@ -95,7 +97,27 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds_wa
 // granule holds pieces x and 2 + x (8 bytes each) of the chunk.
 __device__ __forceinline__ int perm_src(int G, int w4) { return 8 * ((w4 < 2 ? 0 : 2) + (G & 1)) + 4 * (w4 & 1); }
 
-template <bool ISUMS, int KS>
+// 16-byte form of the same load: lane L's 16 bytes at voff go to LDS byte lds_wave_base + 16L.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
+{
+    const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
+    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+}
+
+// Prepared q6_K weights: per 128-row tile T and super-block sb, two 16 KiB stage images
+// (stage hh = weights 128hh..128hh+127 of the super-block) at ((T * nsb + sb) * 2 + hh) *
+// 16 KiB, each laid out exactly as StageLds::bl | bh | dsc (contiguous there): the ql half
+// and the qh half with the 8-byte piece swap and the row swizzle applied, then d*sc of the
+// stage's 8 sub-blocks in C-register row order. Rows past N are zero.
+constexpr int PREP_STAGE = 16384;
+static_assert(offsetof(StageLds, bh) == offsetof(StageLds, bl) + TN * 64 &&
+                  offsetof(StageLds, dsc) == offsetof(StageLds, bh) + TN * 32 &&
+                  sizeof(StageLds::bl) + sizeof(StageLds::bh) + sizeof(StageLds::dsc) == PREP_STAGE,
+              "stage image = bl | bh | dsc");
+
+// PREP: W is the prepared layout (16-byte aligned, no register staging, the q8 tile in
+// natural order by 16-byte loads and its operands read as two 8-byte halves).
+template <bool ISUMS, int KS, bool PREP>
 __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
     float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total)
@@ -115,8 +137,10 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     // Buffer descriptors over this tile's rows: loads past the last token / weight row
     // return zeros.
     const int rows_w = min(TN, N - n0), rows_t = min(TM, M - m0);
-    const __amdgpu_buffer_rsrc_t rW =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * wrow), 0, rows_w * wrow, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rW = PREP
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n_tile * nsb * 2 * PREP_STAGE), 0, nsb * 2 * PREP_STAGE,
+                                            0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)(W + (size_t)n0 * wrow), 0, rows_w * wrow, 0x00020000);
     const __amdgpu_buffer_rsrc_t rQ =
         __builtin_amdgcn_make_buffer_rsrc((void*)(qplane + (size_t)m0 * K), 0, rows_t * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rH =
@@ -134,11 +158,28 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     }
     // q8_1 header words of the stage: wave w brings chunk w of the stage, lane = token.
     const int voH = lane * nc * 4 + 4 * wave;
+    // Prepared path: the q8 tile in natural order by 16-byte loads, slab i = tokens
+    // 8i..8i+7 (8 lanes each), wave w slabs 2w, 2w+1; granule G of token t at slot
+    // G ^ aq_sw(t). Weights: the stage image, 16 slabs of 1 KiB, wave w slabs 4w..4w+3.
+    int voQ16[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int t = 8 * (2 * wave + i) + (lane >> 3);
+        voQ16[i] = t * K + 16 * ((lane & 7) ^ aq_sw(t));
+    }
     auto issue_q8 = [&](int sb, int hh, StageLds& st) {
         const int off = sb * QK_K + hh * HALF;
+        if constexpr (PREP) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-            lds_load4(rQ, st.aq + 256 * (wave + 4 * m), voQ[m & 1] + 8 * m * K + off);
+            for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ16[i] + off);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                lds_load16(rW, st.bl + 1024 * (4 * wave + i), (sb * 2 + hh) * PREP_STAGE + 1024 * (4 * wave + i) + 16 * lane);
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+                lds_load4(rQ, st.aq + 256 * (wave + 4 * m), voQ[m & 1] + 8 * m * K + off);
+        }
         if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
     };
 
@@ -243,10 +284,18 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
                 __builtin_amdgcn_sched_barrier(0);
-                const uint32x4 bq = *reinterpret_cast<const uint32x4*>(st.aq + 128 * (32 * ts + l32) +
-                                                                        16 * ((2 * cl + hg) ^ tsw));
-                const long b0 = (long)(((unsigned long)bq[1] << 32) | bq[0]);
-                const long b1 = (long)(((unsigned long)bq[3] << 32) | bq[2]);
+                long b0, b1;
+                if constexpr (PREP) {
+                    // natural order: piece hg in granule 2cl, piece 2+hg in granule 2cl+1
+                    const uint8_t* row = st.aq + 128 * (32 * ts + l32) + 8 * hg;
+                    b0 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl) ^ tsw));
+                    b1 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl + 1) ^ tsw));
+                } else {
+                    const uint32x4 bq = *reinterpret_cast<const uint32x4*>(st.aq + 128 * (32 * ts + l32) +
+                                                                            16 * ((2 * cl + hg) ^ tsw));
+                    b0 = (long)(((unsigned long)bq[1] << 32) | bq[0]);
+                    b1 = (long)(((unsigned long)bq[3] << 32) | bq[2]);
+                }
                 const int32x16 F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, magic, 0, 0, 0);
                 const int32x16 F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, b1, magic, 0, 0, 0);
                 if constexpr (ISUMS) {
@@ -292,10 +341,13 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
     const int nst = 2 * cnt, nst_all = 2 * (nbase + (nrem ? 1 : 0));
     Pre pre;
+    (void)pre;
     if (nst > 0) {
         issue_q8(sb0, 0, G.st[0]);
-        load_stage(sb0, 0, pre);
-        commit(pre, sb0, G.st[0]);
+        if constexpr (!PREP) {
+            load_stage(sb0, 0, pre);
+            commit(pre, sb0, G.st[0]);
+        }
     }
     for (int h = 0; h < nst_all; ++h) {
         const int sb = sb0 + (h >> 1), hh = h & 1, cur = h & 1;
@@ -305,10 +357,11 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
         const int sbn = sb0 + ((h + 1) >> 1), hhn = (h + 1) & 1;
         if (next) {
             issue_q8(sbn, hhn, G.st[cur ^ 1]);
-            load_stage(sbn, hhn, pre);
+            if constexpr (!PREP) load_stage(sbn, hhn, pre);
         }
         if (h < nst) compute_stage(sb, hh, G.st[cur]);
-        if (next) commit(pre, sbn, G.st[cur ^ 1]);
+        if constexpr (!PREP)
+            if (next) commit(pre, sbn, G.st[cur ^ 1]);
     }
 
     if constexpr (!ISUMS && KS > 1) {
@@ -364,11 +417,63 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     }
 }
 
+// Repack raw q6_K blocks into the prepared layout: workgroup (T, sb), thread (row j =
+// tid & 127, stage hh = tid >> 7) writes row j's part of stage image hh. Rows start only
+// 2-byte aligned, so the bytes are read as aligned dwords and shifted with v_alignbyte.
+__global__ void __launch_bounds__(256) q6K_prepare_kernel(const uint8_t* __restrict__ W, uint8_t* __restrict__ WP,
+                                                          int N, int K)
+{
+    const int nsb = K / QK_K, wrow = nsb * Q6K_BYTES;
+    const int T = (int)(blockIdx.x / (unsigned)nsb), sb = (int)(blockIdx.x % (unsigned)nsb);
+    const int j = threadIdx.x & 127, hh = threadIdx.x >> 7, n = T * TN + j;
+    uint32_t ql[16], qh[8];
+    float dsc[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ql[i] = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { qh[i] = 0u; dsc[i] = 0.0f; }
+    if (n < N) {
+        const uint8_t* blk = W + (size_t)n * wrow + (size_t)sb * Q6K_BYTES;
+        const uint32_t sh = (uint32_t)((uintptr_t)blk & 2);
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(blk + 64 * hh - sh);        // ends by blk + 132
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ql[i] = __builtin_amdgcn_alignbyte(a[i + 1], a[i], sh);
+        const uint32_t* b = reinterpret_cast<const uint32_t*>(blk + 128 + 32 * hh - sh);   // ends by blk + 196
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qh[i] = __builtin_amdgcn_alignbyte(b[i + 1], b[i], sh);
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(blk + 192 + 8 * hh - sh);
+        const uint32_t c2 = sh ? c[2] : 0u;                                                  // ends at blk + 210
+        const uint32_t s0 = __builtin_amdgcn_alignbyte(c[1], c[0], sh), s1 = __builtin_amdgcn_alignbyte(c2, c[1], sh);
+        const float d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk + 208));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dsc[u] = d * (float)(int)(int8_t)((u < 4 ? s0 : s1) >> (8 * (u & 3)));   // exact
+    }
+    uint8_t* img = WP + ((size_t)(T * nsb + sb) * 2 + hh) * PREP_STAGE;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const uint32x4 v = {ql[8 * g + 2 * x], ql[8 * g + 2 * x + 1], ql[8 * g + 4 + 2 * x], ql[8 * g + 5 + 2 * x]};
+            *reinterpret_cast<uint32x4*>(img + 64 * j + 16 * ((2 * g + x) ^ bl_sw(j))) = v;
+        }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const uint32x4 v = {qh[2 * x], qh[2 * x + 1], qh[4 + 2 * x], qh[5 + 2 * x]};
+        *reinterpret_cast<uint32x4*>(img + TN * 64 + 32 * j + 16 * (x ^ bh_sw(j))) = v;
+    }
+    float* dp = reinterpret_cast<float*>(img + TN * 96);
+    const int pos = 32 * (j >> 5) + c_pos(j & 31);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dp[u * TN + pos] = dsc[u];
+}
+
 }  // namespace q6k
 }  // namespace qpg
 
-hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
-                              int64_t K, hipStream_t s)
+namespace {
+template <bool PREP>
+hipError_t launch_q6K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N, int64_t K,
+                      hipStream_t s)
 {
     using namespace qpg::q6k;
     const int tiles_m = (int)((M + TM - 1) / TM);
@@ -381,18 +486,40 @@ hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* 
     const bool split = total <= 256 && K / 256 >= 3;
     if (isums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_kernel<true, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 3, PREP>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total);
         else
-            hipLaunchKernelGGL((mmq_q6K_kernel<true, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 1, PREP>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_kernel<false, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 3, PREP>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total);
         else
-            hipLaunchKernelGGL((mmq_q6K_kernel<false, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 1, PREP>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total);
     }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
+                              int64_t K, hipStream_t s)
+{
+    return launch_q6K<false>(w, xq, y, isums, M, N, K, s);
+}
+
+hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t s)
+{
+    return launch_q6K<true>(wp, xq, y, isums, M, N, K, s);
+}
+
+hipError_t qpg_launch_q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, hipStream_t s)
+{
+    using namespace qpg::q6k;
+    const int64_t tiles_n = (N + TN - 1) / TN;
+    hipLaunchKernelGGL(q6K_prepare_kernel, dim3((unsigned)(tiles_n * (K / 256))), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(w), static_cast<uint8_t*>(wp), (int)N, (int)K);
     return hipGetLastError();
 }

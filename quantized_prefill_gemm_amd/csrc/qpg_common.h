@@ -55,3 +55,7 @@ hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* 
                               int64_t M, int64_t N, int64_t K, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums,
                               int64_t M, int64_t N, int64_t K, hipStream_t s);
+// q6_K prepared layout: ceil(N/128) * (K/256) * 32 KiB (layout in mmq_q6k.hip)
+hipError_t qpg_launch_q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, hipStream_t s);
+hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int32_t* isums,
+                                   int64_t M, int64_t N, int64_t K, hipStream_t s);

@@ -35,8 +35,12 @@ def L():
     lib.quantize_q8_1.argtypes = [P, P, I64, I64, P]
     for f in (lib.mmq_q4K, lib.mmq_q6K):
         f.argtypes = [P, P, P, I64, I64, I64, P, P]
-    for f in (lib.mmq_q4K_q8, lib.mmq_q6K_q8, lib.mmq_q4K_isums, lib.mmq_q6K_isums):
+    for f in (lib.mmq_q4K_q8, lib.mmq_q6K_q8, lib.mmq_q4K_isums, lib.mmq_q6K_isums, lib.mmq_q6K_prep_q8,
+              lib.mmq_q6K_prep_isums):
         f.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.qpg_q6K_prep_bytes.restype = ctypes.c_size_t
+    lib.qpg_q6K_prep_bytes.argtypes = [I64, I64]
+    lib.q6K_prepare.argtypes = [P, P, I64, I64, P]
     return lib
 
 
@@ -85,7 +89,8 @@ def test_quantize_rejects(L, args, expect):
     assert L.quantize_q8_1(*args, None) == expect
 
 
-@pytest.mark.parametrize("fn", ["mmq_q4K_q8", "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums"])
+@pytest.mark.parametrize("fn", ["mmq_q4K_q8", "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums", "mmq_q6K_prep_q8",
+                                "mmq_q6K_prep_isums"])
 @pytest.mark.parametrize("args,expect", [
     ((None, A16, A16, 64, 256, 256), EINVAL),
     ((A16, None, A16, 64, 256, 256), EINVAL),
@@ -110,6 +115,23 @@ def test_alignment_rules_per_type(L):
     assert L.mmq_q6K(A16, A16, A16, 64, 256, 256, None, None) == EINVAL   # missing workspace
 
 
+def test_q6K_prepare_sizes_and_rejects(L):
+    # 32 KiB per (128-row tile, super-block)
+    assert L.qpg_q6K_prep_bytes(4096, 11008) == 32 * 43 * 32768
+    assert L.qpg_q6K_prep_bytes(129, 256) == 2 * 1 * 32768
+    assert L.qpg_q6K_prep_bytes(1, 512) == 2 * 32768
+    for n, k in ((0, 256), (128, 0), (128, 300), (128, 128), (1 << 31, 256), (128, 1 << 24)):
+        assert L.qpg_q6K_prep_bytes(n, k) == 0
+    assert L.q6K_prepare(None, A16, 128, 256, None) == EINVAL
+    assert L.q6K_prepare(A16, None, 128, 256, None) == EINVAL
+    assert L.q6K_prepare(A16, A16, 0, 256, None) == EINVAL
+    assert L.q6K_prepare(A16, A16, 128, 288, None) == EINVAL
+    assert L.q6K_prepare(A2, A16, 128, 256, None) == EALIGN     # raw blocks need 4-byte alignment
+    assert L.q6K_prepare(A16, A8, 128, 256, None) == EALIGN     # prepared layout needs 16
+    assert L.mmq_q6K_prep_q8(A8, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 1 << 24, None) == EINVAL
+
+
 def _has_gpu():
     try:
         import torch
@@ -124,3 +146,5 @@ def test_valid_call_without_device_reports_edevice(L):
     # nothing is enqueued.
     assert L.mmq_q4K_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
     assert L.quantize_q8_1(A16, A16, 64, 256, None) == EDEVICE
+    assert L.q6K_prepare(A16, A16, 128, 256, None) == EDEVICE
+    assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE

@@ -191,6 +191,49 @@ def test_metamorphic(wtype):
     assert np.array_equal(gpu_isums(wtype, W, xq_n, M, N, K), -gpu_isums(wtype, W, xq_p, M, N, K))
 
 
+# ----------------------------------------------------------------------------- prepared q6_K
+
+def gpu_prepare(W, N, K):
+    wp = B.q6K_prepare(dev(W.reshape(-1)), N, K)
+    torch.cuda.synchronize()
+    return wp
+
+
+@pytest.mark.parametrize("M,N,K", ISUM_SHAPES)
+def test_q6K_prep_isums_bitexact(M, N, K):
+    say(f"[q6_K prepared isums {M}x{N}x{K}]")
+    W, X = inputs.small_case("q6_K", M, N, K, seed=3)
+    xq, (q, _, _) = gpu_quantize(X)
+    s = B.mmq_q6K_prep_isums(gpu_prepare(W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), O.isums("q6_K", W, q))
+
+
+@pytest.mark.parametrize("M,N,K", TAIL_SHAPES)
+def test_q6K_prep_tails(M, N, K):
+    say(f"[q6_K prepared mmq {M}x{N}x{K}]")
+    W, X = inputs.small_case("q6_K", M, N, K, seed=5, gain=True)
+    xq, _ = gpu_quantize(X)
+    y = B.mmq_q6K_prep_q8(gpu_prepare(W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq("q6_K", W, X), f"prep {M}x{N}x{K}")
+
+
+def test_q6K_prep_config4_full():
+    wtype, M, N, K, W, X = inputs.make_config(4)
+    say(f"[q6_K prepared cfg4 {M}x{N}x{K}]")
+    xq, _ = gpu_quantize(X)
+    wp = gpu_prepare(W, N, K)
+    y = B.mmq_q6K_prep_q8(wp, xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq(wtype, W, X), "prep cfg4")
+    rows = slice(0, 256)
+    Wr = np.ascontiguousarray(W[rows])
+    s = B.mmq_q6K_prep_isums(gpu_prepare(Wr, 256, K), xq, M, 256, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), gpu_isums(wtype, Wr, xq, M, 256, K))
+
+
 def test_closed_form_scale_path_on_gpu():
     """All nib = 1, sc = 1, d = 1, X = 1: Y = K * 0.99993896484375 exactly (golden)."""
     K = 1024
