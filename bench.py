@@ -67,10 +67,13 @@ def setup(cfg: int):
     return B, wtype, M, N, K, W, X, w, x, y, ws
 
 
-def run_gpu(cfg: int, steps: int, warmup: int):
+def run_gpu(cfg: int, steps: int, warmup: int, prepared: bool = False):
     import torch
     B, wtype, M, N, K, W, X, w, x, y, ws = setup(cfg)
     mmq_q8 = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
+    if prepared and wtype == "q6_K":
+        w = B.q6K_prepare(w, N, K)          # one-time repack, outside the timed region
+        mmq_q8 = B.mmq_q6K_prep_q8
     stream = torch.cuda.current_stream()
 
     def step():
@@ -111,6 +114,110 @@ def cpu_baseline(wtype, W, X):
                       f"{dt:.2f} s wall on {nth} threads"}
 
 
+def run_stack(steps: int, warmup: int, prepared: bool):
+    """Config 5: the 32-layer 7B-shaped stack at M = 1024, each of the 7 GEMMs of a layer
+    preceded by its quantize_q8_1, captured as one HIP graph of 448 launches (torch's graph
+    API over the library's own launches) and replayed. Weights: the seeded per-layer
+    generator (4.15 GB of q4_K / q6_K blocks resident in HBM); activations: one seeded input
+    per matrix position, reused by every layer."""
+    import torch
+    from quantized_prefill_gemm_amd import binding as B
+    from quantized_prefill_gemm_amd import inputs
+    M, L = inputs.STACK_M, inputs.STACK_LAYERS
+    dev = torch.device("cuda:0")
+    mats = []
+    for layer in range(L):
+        for idx in range(len(inputs.STACK_LAYER)):
+            name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
+            w = torch.from_numpy(W.reshape(-1)).to(dev)
+            if wtype == "q6_K" and prepared:
+                w = B.q6K_prepare(w, N, K)
+            mats.append((idx, wtype, N, K, w))
+        torch.cuda.synchronize()
+        if layer % 8 == 7:
+            print(f"stack weights: {layer + 1}/{L} layers resident", file=sys.stderr, flush=True)
+    xs, xqs, ys = {}, {}, {}
+    for idx, (name, wtype, N, K) in enumerate(inputs.STACK_LAYER):
+        xs[idx] = torch.from_numpy(inputs.make_stack_input(0, idx)).to(dev)
+        xqs[idx] = torch.empty(B.q8_1_bytes(M, K), dtype=torch.uint8, device=dev)
+        ys[idx] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    # q, k, v read the same hidden state and gate, up the same normed state: with
+    # quantize sharing, one quantize serves each group (4 per layer instead of 7)
+    share_src = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}
+
+    def mmq(idx, wtype, N, K, w, xq):
+        if wtype == "q4_K":
+            B.mmq_q4K_q8(w, xq, M, N, K, ys[idx])
+        elif prepared:
+            B.mmq_q6K_prep_q8(w, xq, M, N, K, ys[idx])
+        else:
+            B.mmq_q6K_q8(w, xq, M, N, K, ys[idx])
+
+    def pass_(mode):
+        for idx, wtype, N, K, w in mats:
+            if mode == "all":
+                B.quantize_q8_1(xs[idx], xqs[idx])
+                mmq(idx, wtype, N, K, w, xqs[idx])
+            elif mode == "shared":
+                src = share_src[idx]
+                if src == idx:
+                    B.quantize_q8_1(xs[idx], xqs[idx])
+                mmq(idx, wtype, N, K, w, xqs[src])
+            else:                                   # "gemm": the GEMMs alone
+                mmq(idx, wtype, N, K, w, xqs[idx])
+
+    for idx in xs:
+        B.quantize_q8_1(xs[idx], xqs[idx])
+    torch.cuda.synchronize()
+    res = {}
+    for mode in ("all", "shared", "gemm"):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            pass_(mode)                              # eager warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            pass_(mode)
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        res[mode] = ms[len(ms) // 2]
+        print(f"stack graph '{mode}': median {res[mode]:.3f} ms per pass", file=sys.stderr, flush=True)
+        del g
+    macs = M * L * sum(N * K for _, _, N, K in inputs.STACK_LAYER)
+    return macs, res
+
+
+def stack_cpu_baseline():
+    """Oracle on each distinct GEMM shape of the stack at M = 1024 once (plus the
+    quantize it includes), extrapolated with the multiplicities 3 / 1 / 2 / 1 x 32 layers."""
+    from oracle import oracle as O
+    from quantized_prefill_gemm_amd import inputs
+    nth = O.default_threads()
+    per = {}
+    for idx in (0, 2, 4, 6):
+        name, wtype, N, K, W = inputs.make_stack_matrix(0, idx)
+        X = inputs.make_stack_input(0, idx)
+        t0 = time.perf_counter()
+        O.mmq(wtype, W, X, nthreads=nth)
+        per[idx] = time.perf_counter() - t0
+    total = inputs.STACK_LAYERS * (3 * per[0] + per[2] + 2 * per[4] + per[6])
+    macs = inputs.STACK_M * inputs.STACK_LAYERS * sum(N * K for _, _, N, K in inputs.STACK_LAYER)
+    return {"value": macs / total / 1e12, "unit": "TMAC/s", "cores": nth, "kind": "oracle",
+            "sample": "the 4 distinct GEMM shapes of layer 0 at M=1024 once each (quantize + exact int32 "
+                      f"sums + fp64 fold), {sum(per.values()):.2f} s, extrapolated x(3,1,2,1) x 32 layers "
+                      f"to {total:.1f} s"}
+
+
 def profile_mode(which: str, launches: int):
     import torch
     cfg = {"q4K": 3, "q6K": 4, "quant": 3}[which]
@@ -141,7 +248,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, help="workload 2/3 (q4_K) or 4 (q6_K)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 2/3 (q4_K), 4 (q6_K) or 5 (the 32-layer stack as one graph)")
+    ap.add_argument("--prepared", action="store_true",
+                    help="q6_K weights through the one-time prepare pass (config 4; always used for 5 "
+                         "unless --raw-q6k)")
+    ap.add_argument("--raw-q6k", action="store_true", help="config 5: q6_K GEMMs on raw blocks")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile", choices=["q4K", "q6K", "quant"])
     ap.add_argument("--launches", type=int, default=20)
@@ -158,7 +270,30 @@ def main():
         profile_mode(a.profile, a.launches)
         return
 
-    r = run_gpu(a.config, a.steps, a.warmup)
+    if a.config == 5:
+        steps = a.steps if a.steps != ap.get_default("steps") else 10
+        warmup = a.warmup if a.warmup != ap.get_default("warmup") else 2
+        macs, res = run_stack(steps, warmup, prepared=not a.raw_q6k)
+        ms = res["all"]
+        out = {
+            "metric": METRIC, "value": round(macs / (ms * 1e-3) / 1e12, 3), "unit": "TMAC/s", "n_gpus": 1,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+            "config": {"workload": "32-layer 7B-shaped stack, M=1024: q/k/o 4096x4096 q4_K, v 4096x4096 q6_K, "
+                                   "gate/up 11008x4096 q4_K, down 4096x11008 q6_K, quantize_q8_1 before each "
+                                   "GEMM; one HIP graph of 448 launches",
+                       "M": 1024, "layers": 32, "q6_K": "raw blocks" if a.raw_q6k else "prepared"},
+            "stack_ms": {k: round(v, 4) for k, v in res.items()},
+            "stack_tmacs": {"with_7_quantizes": round(macs / (res["all"] * 1e-3) / 1e12, 3),
+                            "with_4_shared_quantizes": round(macs / (res["shared"] * 1e-3) / 1e12, 3),
+                            "gemms_only": round(macs / (res["gemm"] * 1e-3) / 1e12, 3)},
+        }
+        if not a.no_cpu:
+            out["cpu_baseline"] = stack_cpu_baseline()
+        print(json.dumps(out), flush=True)
+        return
+
+    r = run_gpu(a.config, a.steps, a.warmup, prepared=a.prepared)
     M, N, K = r["M"], r["N"], r["K"]
     macs = M * N * K
     ms_step = r["span_ms"] / a.steps
@@ -180,7 +315,9 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": f"{r['wtype']} MMQ + q8_1 quantize, M={M} tokens x N={N} x K={K}"
-                               + (" (FFN gate/up shape, per-token gains U[0.5,2])" if a.config == 3 else ""),
+                               + (" (FFN gate/up shape, per-token gains U[0.5,2])" if a.config == 3 else "")
+                               + (" (q6_K weights prepared once, outside the timed steps)"
+                                  if a.prepared and r["wtype"] == "q6_K" else ""),
                    "M": M, "N": N, "K": K, "weights": r["wtype"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 5), "traffic": traffic,
