@@ -255,3 +255,55 @@ def test_stack_sampled_rows():
             rows = np.sort(rng.choice(N, 16, replace=False))
             r = O.mmq(wtype, W[rows], X)
             check_out(g[:, rows], r, f"stack L{layer} {name}")
+
+
+def test_graph_replay_matches_eager():
+    """A small two-layer stack (quantize + q4_K / q6_K / prepared q6_K GEMMs) captured as one
+    graph: every replay, with eager work and synchronisations between replays, must give
+    the eager outputs bit for bit."""
+    M = 96
+    specs = [("q4_K", 384, 512), ("q6_K", 256, 768), ("q6p", 200, 1024), ("q4_K", 130, 768)]
+    mats, xs, xqs, ys = [], [], [], []
+    for i, (kind, N, K) in enumerate(specs):
+        wtype = "q4_K" if kind == "q4_K" else "q6_K"
+        W, X = inputs.small_case(wtype, M, N, K, seed=40 + i)
+        w = dev(W.reshape(-1))
+        if kind == "q6p":
+            w = B.q6K_prepare(w, N, K)
+        mats.append((kind, N, K, w))
+        xs.append(dev(X))
+        xqs.append(torch.empty(B.q8_1_bytes(M, K), dtype=torch.uint8, device=DEV))
+        ys.append(torch.empty((M, N), dtype=torch.float32, device=DEV))
+
+    def run():
+        for (kind, N, K, w), x, xq, y in zip(mats, xs, xqs, ys):
+            B.quantize_q8_1(x, xq)
+            if kind == "q4_K":
+                B.mmq_q4K_q8(w, xq, M, N, K, y)
+            elif kind == "q6_K":
+                B.mmq_q6K_q8(w, xq, M, N, K, y)
+            else:
+                B.mmq_q6K_prep_q8(w, xq, M, N, K, y)
+
+    say("[graph replay]")
+    run()
+    torch.cuda.synchronize()
+    ref = [y.cpu().numpy().copy() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        run()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, y in enumerate(ys):
+            assert np.array_equal(y.cpu().numpy(), ref[i]), f"replay {rep}, GEMM {i}"
+
