@@ -49,6 +49,7 @@ namespace qpg {
 namespace q4k {
 
 typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned uint32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TM = 64;            // tokens per workgroup tile
@@ -96,19 +97,6 @@ __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_
 // Position of weight row jj (0..31 inside a wave's rows) in C-register order: k-group
 // (jj >> 2) & 1 holds registers r = 4*(jj >> 3) + (jj & 3).
 __device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
-
-__device__ __forceinline__ void split3_bf16(float v, uint16_t* dst, int stride)
-{
-    // v = b1 + b2 + b3 exactly for v with <= 24 significant bits
-    const uint32_t b1 = f32_to_bf16_bits(v);
-    const float r1 = v - bf16_bits_to_f32(b1);
-    const uint32_t b2 = f32_to_bf16_bits(r1);
-    const float r2 = r1 - bf16_bits_to_f32(b2);
-    const uint32_t b3 = f32_to_bf16_bits(r2);
-    dst[0] = (uint16_t)b1;
-    dst[stride] = (uint16_t)b2;
-    dst[2 * stride] = (uint16_t)b3;
-}
 
 // Wait until this wave's outstanding vector-memory operations (the LDS-direct loads) are
 // complete: vmcnt(0), expcnt and lgkmcnt left at their maxima.
@@ -214,36 +202,52 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
     // into the fold terms.
     auto decode_headers = [&](const uint32x4 hv) {
         if (tid < TN) {
+            // bytewise unpack of the 12 packed bytes: byte s of each word is sub-block s (s < 4)
+            // or s + 4 (the high nibbles of S2 plus the top two bits of S0 / S1)
             const int j = tid;
             const float d = half_bits_to_float(hv[0] & 0xFFFFu);
             const float dmin = half_bits_to_float(hv[0] >> 16);
             const uint32_t S0 = hv[1], S1 = hv[2], S2 = hv[3];
+            const uint32_t sc03 = S0 & 0x3F3F3F3Fu, m03 = S1 & 0x3F3F3F3Fu;
+            const uint32_t sc47 = (S2 & 0x0F0F0F0Fu) | ((S0 >> 2) & 0x30303030u);
+            const uint32_t m47 = ((S2 >> 4) & 0x0F0F0F0Fu) | ((S1 >> 2) & 0x30303030u);
             const int pos = 32 * (j >> 5) + c_pos(j & 31);
             L.bnd[pos] = -dmin;
+            uint32_t mb[8];
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                uint32_t sc, m;
-                if (s < 4) {
-                    sc = (S0 >> (8 * s)) & 63u;
-                    m = (S1 >> (8 * s)) & 63u;
-                } else {
-                    const int s4 = 8 * (s - 4);
-                    sc = ((S2 >> s4) & 15u) | (((S0 >> s4) >> 6 & 3u) << 4);
-                    m = ((S2 >> s4) >> 4 & 15u) | (((S1 >> s4) >> 6 & 3u) << 4);
-                }
-                L.dsv[s][pos] = d * (float)sc;                      // exact (17 bits)
-                L.bw[j * 8 + s] = (uint16_t)(__float_as_uint((float)m) >> 16);
+                const uint32_t scw = s < 4 ? sc03 : sc47, mw = s < 4 ? m03 : m47;
+                const int b = 8 * (s & 3);
+                L.dsv[s][pos] = d * (float)((scw >> b) & 0xFFu);           // exact (17 bits)
+                mb[s] = __float_as_uint((float)((mw >> b) & 0xFFu));         // exact bf16 in the high half
             }
+            const uint32x4 mw4 = {(mb[0] >> 16) | (mb[1] & 0xFFFF0000u), (mb[2] >> 16) | (mb[3] & 0xFFFF0000u),
+                                  (mb[4] >> 16) | (mb[5] & 0xFFFF0000u), (mb[6] >> 16) | (mb[7] & 0xFFFF0000u)};
+            *reinterpret_cast<uint32x4*>(L.bw + j * 8) = mw4;
         } else {
+            // per chunk: da, -1.5*2^23*da, and da*ssum split into three bf16 pieces by
+            // truncation (each piece keeps the top 8 significant bits of what is left; 24 bits
+            // in, so the third remainder is itself a bf16 and the pieces sum exactly)
             const int u = tid - TN, t = u >> 1, c4 = 4 * (u & 1);
+            uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int c = c4 + e;
                 const uint32_t hw = hv[e];
                 const float da = half_bits_to_float(hw & 0xFFFFu);
-                L.ada[c][t] = make_float2(da, -MAGIC_F * da);       // exact
-                split3_bf16(da * (float)(int16_t)(hw >> 16), L.ax + t * PC_STRIDE + c, 8);   // da*ssum exact
+                L.ada[c4 + e][t] = make_float2(da, -MAGIC_F * da);        // exact
+                const float v = da * (float)(int)(int16_t)(hw >> 16);       // da*ssum exact (23 bits)
+                const float b1 = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
+                const float r1 = v - b1;                                     // exact
+                const float b2 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
+                const float r2 = r1 - b2;                                    // exact, <= 8 significant bits
+                p1[e] = __float_as_uint(b1);
+                p2[e] = __float_as_uint(b2);
+                p3[e] = __float_as_uint(r2);
             }
+            uint16_t* axr = L.ax + t * PC_STRIDE + c4;
+            *reinterpret_cast<uint32x2*>(axr) = uint32x2{(p1[0] >> 16) | (p1[1] & 0xFFFF0000u), (p1[2] >> 16) | (p1[3] & 0xFFFF0000u)};
+            *reinterpret_cast<uint32x2*>(axr + 8) = uint32x2{(p2[0] >> 16) | (p2[1] & 0xFFFF0000u), (p2[2] >> 16) | (p2[3] & 0xFFFF0000u)};
+            *reinterpret_cast<uint32x2*>(axr + 16) = uint32x2{(p3[0] >> 16) | (p3[1] & 0xFFFF0000u), (p3[2] >> 16) | (p3[3] & 0xFFFF0000u)};
         }
     };
 
