@@ -6,7 +6,9 @@ q4_K MMQ against W [11008 x 4096] q4_K, output Y [512 x 11008] f32. Inputs are s
 synthetic data resident in HBM before timing starts.
 
 Prints ONE JSON line (metric, value in TMAC/s = M*N*K / step time, roofline of the MMQ
-kernel, CPU-oracle baseline). Other modes (for rocprofv3 runs):
+kernel, CPU-oracle baseline). Defaults: 200 warm-up and 1000 timed steps (~100 ms of GPU
+time): the first ~10-20 ms of a run are up to 10 % slower while the clock ramps up.
+Other modes (for rocprofv3 runs):
   --profile {q4K,q6K,quant}  a few launches of one kernel, no timing output
   --copy-calibration         a device-to-device copy of known size (HBM counter scale)
 """
@@ -83,22 +85,29 @@ def run_gpu(cfg: int, steps: int, warmup: int, prepared: bool = False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
+
+    def bracketed(fn, n):
+        """Average over n back-to-back calls, HIP events on the launch stream around them all
+        (an event between two launches costs ~3 us of GPU time on this device, so none is
+        recorded inside)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    # timed region: exactly `steps` steps
     t0 = time.perf_counter()
-    for i in range(steps):
-        ev[i][0].record(stream)
-        B.quantize_q8_1(x, ws, stream=stream)
-        ev[i][1].record(stream)
-        mmq_q8(w, ws, M, N, K, y, stream=stream)
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
+    step_ms = bracketed(step, steps)
     wall = time.perf_counter() - t0
-    q_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]
-    m_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]
-    span_ms = ev[0][0].elapsed_time(ev[-1][2])
-    return dict(wtype=wtype, M=M, N=N, K=K, W=W, X=X, wall_s=wall, span_ms=span_ms,
-                quant_ms=sum(q_ms) / steps, mmq_ms=sum(m_ms) / steps, mmq_min_ms=min(m_ms))
+    # per-kernel averages, the same launches back to back, right after the timed steps
+    mmq_ms = bracketed(lambda: mmq_q8(w, ws, M, N, K, y, stream=stream), steps)
+    quant_ms = bracketed(lambda: B.quantize_q8_1(x, ws, stream=stream), steps)
+    return dict(wtype=wtype, M=M, N=N, K=K, W=W, X=X, wall_s=wall, step_ms=step_ms,
+                quant_ms=quant_ms, mmq_ms=mmq_ms)
 
 
 def cpu_baseline(wtype, W, X):
@@ -116,8 +125,8 @@ def cpu_baseline(wtype, W, X):
 
 def run_stack(steps: int, warmup: int, prepared: bool):
     """Config 5: the 32-layer 7B-shaped stack at M = 1024, each of the 7 GEMMs of a layer
-    preceded by its quantize_q8_1, captured as one HIP graph of 448 launches (torch's graph
-    API over the library's own launches) and replayed. Weights: the seeded per-layer
+    preceded by its quantize_q8_1: 448 launches per pass, timed both as one HIP graph (torch's
+    graph API over the library's own launches) replayed, and launched eagerly. Weights: the seeded per-layer
     generator (4.15 GB of q4_K / q6_K blocks resident in HBM); activations: one seeded input
     per matrix position, reused by every layer."""
     import torch
@@ -190,9 +199,23 @@ def run_stack(steps: int, warmup: int, prepared: bool):
             e1.record()
         torch.cuda.synchronize()
         ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
-        res[mode] = ms[len(ms) // 2]
-        print(f"stack graph '{mode}': median {res[mode]:.3f} ms per pass", file=sys.stderr, flush=True)
+        res[mode + "_graph"] = ms[len(ms) // 2]
         del g
+        # the same pass launched eagerly (the host stays ahead of the GPU: ~15 us per launch
+        # against ~60 us per kernel), timed as a whole
+        for _ in range(warmup):
+            pass_(mode)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            pass_(mode)
+        e1.record()
+        torch.cuda.synchronize()
+        res[mode + "_eager"] = e0.elapsed_time(e1) / steps
+        res[mode] = min(res[mode + "_graph"], res[mode + "_eager"])
+        print(f"stack '{mode}': graph median {res[mode + '_graph']:.3f} ms, eager mean "
+              f"{res[mode + '_eager']:.3f} ms per pass", file=sys.stderr, flush=True)
     macs = M * L * sum(N * K for _, _, N, K in inputs.STACK_LAYER)
     return macs, res
 
@@ -246,8 +269,8 @@ def copy_calibration(nbytes: int, launches: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=3,
                     help="workload 2/3 (q4_K), 4 (q6_K) or 5 (the 32-layer stack as one graph)")
     ap.add_argument("--prepared", action="store_true",
@@ -281,9 +304,10 @@ def main():
             "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
             "config": {"workload": "32-layer 7B-shaped stack, M=1024: q/k/o 4096x4096 q4_K, v 4096x4096 q6_K, "
                                    "gate/up 11008x4096 q4_K, down 4096x11008 q6_K, quantize_q8_1 before each "
-                                   "GEMM; one HIP graph of 448 launches",
+                                   "GEMM; 448 launches per pass, as one HIP graph or eagerly, whichever is faster",
                        "M": 1024, "layers": 32, "q6_K": "raw blocks" if a.raw_q6k else "prepared"},
             "stack_ms": {k: round(v, 4) for k, v in res.items()},
+            "launch": "graph" if res["all_graph"] <= res["all_eager"] else "eager",
             "stack_tmacs": {"with_7_quantizes": round(macs / (res["all"] * 1e-3) / 1e12, 3),
                             "with_4_shared_quantizes": round(macs / (res["shared"] * 1e-3) / 1e12, 3),
                             "gemms_only": round(macs / (res["gemm"] * 1e-3) / 1e12, 3)},
@@ -296,7 +320,7 @@ def main():
     r = run_gpu(a.config, a.steps, a.warmup, prepared=a.prepared)
     M, N, K = r["M"], r["N"], r["K"]
     macs = M * N * K
-    ms_step = r["span_ms"] / a.steps
+    ms_step = r["step_ms"]
     value = macs / (ms_step * 1e-3) / 1e12
     mmq_s = r["mmq_ms"] * 1e-3
     achieved = 2 * macs / mmq_s / 1e12
@@ -324,7 +348,8 @@ def main():
                      "kernel": f"mmq_{r['wtype'].replace('_', '')}_kernel", "avg_us": round(r["mmq_ms"] * 1e3, 3),
                      "note": "int8 ops counted as 2 per MAC, as in the 5.0 POP/s dense peak"},
         "kernels_us": {"quantize_q8_1": round(r["quant_ms"] * 1e3, 3), "mmq": round(r["mmq_ms"] * 1e3, 3),
-                       "mmq_min": round(r["mmq_min_ms"] * 1e3, 3)},
+                       "timing": "HIP events on the launch stream around K back-to-back launches of "
+                                 "each kernel, right after the K timed steps"},
         "mmq_tmacs": round(macs / mmq_s / 1e12, 3),
         "mmq_hbm_gbs_algorithmic": round(algorithmic_bytes(M, N, K, 144 if r["wtype"] == "q4_K" else 210)
                                          / mmq_s / 1e9, 1),
