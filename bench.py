@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "int8 TMAC/s of q4_K/q6_K MMQ at 7B prefill shapes (M=512); % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s (2 ops per MAC)
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_VALU_TFLOPS = 157.3     # MI355X f32 vector peak (FMA = 2 FLOP)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mmq_q4K_512x11008x4096.txt")
 KERNEL_SOURCES = ["quantized_prefill_gemm_amd/csrc/mmq_q4k.hip", "quantized_prefill_gemm_amd/csrc/qpg_common.h"]
 
@@ -121,6 +122,38 @@ def cpu_baseline(wtype, W, X):
     return {"value": M * N * K / dt / 1e12, "unit": "TMAC/s", "cores": nth, "kind": "oracle",
             "sample": f"full workload {M}x{N}x{K} {wtype}, one run: quantize_q8_1 + exact int32 sums + fp64 fold, "
                       f"{dt:.2f} s wall on {nth} threads"}
+
+
+def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
+    """Measured int8 matrix-core peak and shader clock (libqpg_calib.so: chains of
+    v_mfma_i32_32x32x32_i8 only, two waves per SIMD)."""
+    import ctypes
+    import statistics
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so"))
+    lib.qpg_calib_mfma_i8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qpg_calib_mfma_i8.restype = ctypes.c_int
+    out = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    if lib.qpg_calib_mfma_i8(blocks, 100, ctypes.c_void_p(out.data_ptr()), sp) != 0:
+        raise RuntimeError("qpg_calib_mfma_i8 failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    rc = lib.qpg_calib_mfma_i8(blocks, iters, ctypes.c_void_p(out.data_ptr()), sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    if rc != 0:
+        raise RuntimeError("qpg_calib_mfma_i8 failed")
+    secs = e0.elapsed_time(e1) * 1e-3
+    ops = blocks * 4 * iters * 16 * 65536
+    v = out.view(blocks, 4).cpu().numpy()
+    clocks = [t / (r / 100e6) for t, r in zip(v[:, 0], v[:, 1]) if r > 0]
+    ghz = statistics.median(clocks) / 1e9
+    return {"value": round(ops / secs / 1e12, 1), "unit": "TOP/s", "clock_ghz": round(ghz, 3),
+            "spec_at_this_clock": round(PEAK_INT8_TOPS * ghz / 2.4, 1),
+            "kernel": "v_mfma_i32_32x32x32_i8 chains, 2 waves per SIMD", "seconds": round(secs, 5)}
 
 
 def run_stack(steps: int, warmup: int, prepared: bool):
@@ -355,6 +388,16 @@ def main():
                                          / mmq_s / 1e9, 1),
         "wall_s": round(r["wall_s"], 4),
     }
+    # The fold (2 f32 FMAs per output and 32-chunk for q4_K, 4 for q6_K) runs on the VALU, which
+    # the matrix core does not overlap on this device; its share against the f32 vector peak.
+    fold_fma = M * N * (K // 32) * (2 if r["wtype"] == "q4_K" else 4)
+    fold_tflops = 2 * fold_fma / mmq_s / 1e12
+    out["fold_valu"] = {"achieved": round(fold_tflops, 2), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(fold_tflops / PEAK_F32_VALU_TFLOPS, 4),
+                        "mfma_plus_fold_frac": round(achieved / PEAK_INT8_TOPS + fold_tflops / PEAK_F32_VALU_TFLOPS, 4)}
+    pk = measured_mfma_peak()
+    pk["achieved_frac_of_measured"] = round(achieved / pk["value"], 5)
+    out["mfma_peak_measured"] = pk
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(r["wtype"], r["W"], r["X"])
     print(json.dumps(out), flush=True)

@@ -1,4 +1,5 @@
-"""Build libqpg.so (all HIP sources of csrc/) for gfx950 with hipcc, in-tree."""
+"""Build libqpg.so (all HIP sources of csrc/) and the measurement helper libqpg_calib.so
+(csrc/calib/) for gfx950 with hipcc, in-tree."""
 from __future__ import annotations
 
 import glob
@@ -9,6 +10,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libqpg.so")
 SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+CALIB_LIB = os.path.join(HERE, "libqpg_calib.so")
+CALIB_SOURCES = sorted(glob.glob(os.path.join(HERE, "csrc", "calib", "*.hip")))
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 (packed fp32 forms are kept out of the code).
 # Correctly rounded f32 division is required by the q8_1 scale (d = amax / 127, 1/d).
@@ -27,8 +30,8 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(extra: list[str] | None = None, out: str = LIB, verbose: bool = False) -> str:
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-o", out + ".tmp", *SOURCES]
+def _compile(sources: list[str], out: str, extra: list[str] | None, verbose: bool) -> str:
+    cmd = [hipcc(), *HIPCC_FLAGS, *(extra or []), "-o", out + ".tmp", *sources]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l]
     if res.returncode != 0:
@@ -36,6 +39,13 @@ def build(extra: list[str] | None = None, out: str = LIB, verbose: bool = False)
     if verbose and msgs:
         print("\n".join(msgs), file=sys.stderr)
     os.replace(out + ".tmp", out)
+    return out
+
+
+def build(extra: list[str] | None = None, out: str = LIB, verbose: bool = False) -> str:
+    _compile(SOURCES, out, extra, verbose)
+    if out == LIB:
+        _compile(CALIB_SOURCES, CALIB_LIB, extra, verbose)
     return out
 
 

@@ -148,3 +148,27 @@ def test_valid_call_without_device_reports_edevice(L):
     assert L.quantize_q8_1(A16, A16, 64, 256, None) == EDEVICE
     assert L.q6K_prepare(A16, A16, 128, 256, None) == EDEVICE
     assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
+
+
+CALIB = os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so")
+CALIB_HEADER = os.path.join(ROOT, "include", "qpg_calib.h")
+
+
+def test_calib_library_exports_and_rejects():
+    if not os.path.exists(CALIB):
+        pytest.skip("libqpg_calib.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
+    names = re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    assert names == ["qpg_calib_mfma_i8"]
+    lib = ctypes.CDLL(CALIB)
+    f = lib.qpg_calib_mfma_i8
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(512, 100, None, None) == EINVAL
+    assert f(0, 100, A16, None) == EINVAL
+    assert f(65537, 100, A16, None) == EINVAL
+    assert f(512, 0, A16, None) == EINVAL
+    assert f(512, 10_000_001, A16, None) == EINVAL
+    assert f(512, 100, ctypes.c_void_p((1 << 20) + 4), None) == EALIGN
+    if not _has_gpu():
+        assert f(512, 100, A16, None) == EDEVICE

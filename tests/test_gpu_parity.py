@@ -6,6 +6,7 @@ Bars (from the method's stated targets):
   * f32 outputs: |gpu - oracle| <= 1e-4*|oracle| + 1e-3*rms(oracle) element-wise, the
     oracle being exact up to fp64 summation.
 """
+import os
 import sys
 
 import numpy as np
@@ -307,3 +308,16 @@ def test_graph_replay_matches_eager():
         for i, y in enumerate(ys):
             assert np.array_equal(y.cpu().numpy(), ref[i]), f"replay {rep}, GEMM {i}"
 
+
+
+def test_calib_mfma_peak_runs():
+    # the measurement helper of bench.py: every workgroup reports a positive tick count
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(B.LIB_PATH), "libqpg_calib.so"))
+    lib.qpg_calib_mfma_i8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qpg_calib_mfma_i8.restype = ctypes.c_int
+    out = torch.zeros(256 * 4, dtype=torch.int64, device="cuda:0")
+    assert lib.qpg_calib_mfma_i8(256, 200, ctypes.c_void_p(out.data_ptr()), None) == 0
+    torch.cuda.synchronize()
+    v = out.view(256, 4).cpu().numpy()
+    assert (v[:, 0] > 0).all() and (v[:, 1] > 0).all() and (v[:, 3] == 0).all()
