@@ -161,12 +161,22 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         voB[i] = gb == 4 ? PAD_OFF : (unsigned)(j * wrow + 16 + 16 * gb);
     }
 
+    // The stage offset moves the descriptors' base (scalar arithmetic) instead of every
+    // lane's offset; the range shrinks by the same amount, so the bounds are unchanged.
+    const int8_t* const qbase = qplane + (size_t)m0 * K;
+    const uint8_t* const wbase = W + (size_t)n0 * wrow;
+    const unsigned nQ = (unsigned)(rows_t * K), nW = (unsigned)(rows_w * wrow);
     auto issue_stage = [&](int sb, int hh, uint8_t* aq, uint8_t* bq) {
-        const unsigned oa = sb * QK_K + hh * HALF, ob = sb * Q4K_BYTES + hh * (HALF / 2);
+        const unsigned oa = __builtin_amdgcn_readfirstlane(sb * QK_K + hh * HALF);
+        const unsigned ob = __builtin_amdgcn_readfirstlane(sb * Q4K_BYTES + hh * (HALF / 2));
+        const __amdgpu_buffer_rsrc_t rQs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + oa), 0, (int)(nQ - oa), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rWs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(wbase + ob), 0, (int)(nW - ob), 0x00020000);
 #pragma unroll
         for (int i = 0; i < 3; ++i) {
-            if (i < nA) lds_load16(rQ, aq + 1024 * (i < 2 ? wave + 4 * i : 8), (int)(voA[i] + oa));
-            if (i < nB) lds_load16(rW, bq + 1024 * (i < 2 ? wave + 4 * i : 8 + wave), (int)(voB[i] + ob));
+            if (i < nA) lds_load16(rQs, aq + 1024 * (i < 2 ? wave + 4 * i : 8), (int)voA[i]);
+            if (i < nB) lds_load16(rWs, bq + 1024 * (i < 2 ? wave + 4 * i : 8 + wave), (int)voB[i]);
         }
     };
 
@@ -266,6 +276,7 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         auto ld_b = [&](int cl, int ts) -> int32x4 {
             return *reinterpret_cast<const int32x4*>(aq + aq_base + 4608 * ts + 32 * cl);
         };
+        if constexpr (!ISUMS) asm volatile("" : "+v"(magic));   // keep the constant in VGPRs
         uint32x4 raw = ld_raw(0);
         int32x16 F[2];
         F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, 0), ld_b(0, 0), magic, 0, 0, 0);
