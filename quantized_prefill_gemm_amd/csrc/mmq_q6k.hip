@@ -18,16 +18,16 @@
 //    1.5*2^23 + J exactly (|J| <= 32*127*16 < 2^22): e = fma(F, da, -1.5*2^23*da) is
 //    round(da*J) and y = fma(e, d*sc, y). Two VALU ops per output and sub-block.
 //  * Staging is a two-deep pipeline of half super-blocks (128 k, one barrier per stage).
-//    The q8 tile of stage h+1 comes by dword LDS-direct loads (buffer_load_dword ... lds)
-//    issued before stage h is computed. The weight bytes of stage h+1 (rows start only
+//    The q8 tile of stage h+1 comes by 16-byte LDS-direct loads (buffer_load_dwordx4 ...
+//    lds) in natural order, issued before stage h is computed, and the q8_1 header words
+//    of the stage by dword LDS-direct loads. The weight bytes of stage h+1 (rows start only
 //    2-byte aligned: 210-byte blocks) are fetched into registers as aligned dwords at the
 //    same time, shifted into place with v_alignbyte and written to the other LDS buffer
-//    after stage h's compute, together with d*sc; the q8_1 header words come by dword
-//    LDS-direct loads with the q8 tile.
-//  * LDS: inside every 32-byte group of q, ql and qh the 8-byte pieces 1 and 2 are swapped
-//    (the dword loads pick their source accordingly), so one 16-byte read gives a lane its
-//    8 bytes of both sub-blocks of a chunk (k-group l>>5 of each K=16 MFMA). Rows are
-//    XOR-swizzled in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups.
+//    after stage h's compute, together with d*sc.
+//  * LDS: inside every 32-byte group of ql and qh the 8-byte pieces 1 and 2 are swapped, so
+//    one 16-byte read gives a lane its 8 bytes of both sub-blocks of a chunk (k-group l>>5
+//    of each K=16 MFMA); the matching q8 operand is two 8-byte reads. Rows are XOR-swizzled
+//    in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups.
 //  * When the matrix has at most one tile per CU, three groups of four waves share a
 //    workgroup, each over a contiguous range of super-blocks, and the partial tiles are
 //    added in group order through LDS at the end (three waves per SIMD, deterministic).
@@ -47,7 +47,7 @@ constexpr int TN = 128;
 constexpr int HALF = 128;          // k per pipeline stage
 
 // One pipeline stage (half a super-block) of one group.
-//   aq:  token t at 128 t; granule G (chunk G>>1, k-group G&1, pieces swapped) at slot G ^ ((t >> 1) & 7)
+//   aq:  token t at 128 t; granule G (16 consecutive k) at slot G ^ ((t >> 1) & 7)
 //   bl:  ql half, row j at 64 j; granule G (group G>>1, part G&1) at slot G ^ ((j >> 2) & 3)
 //   bh:  qh half, row j at 32 j; granule G at slot G ^ ((j >> 3) & 1)
 struct StageLds {
@@ -92,10 +92,6 @@ __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds_wa
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
 }
-
-// Source byte, inside a 32-byte chunk, of dword w4 of granule G's half x = G & 1: the
-// granule holds pieces x and 2 + x (8 bytes each) of the chunk.
-__device__ __forceinline__ int perm_src(int G, int w4) { return 8 * ((w4 < 2 ? 0 : 2) + (G & 1)) + 4 * (w4 & 1); }
 
 // 16-byte form of the same load: lane L's 16 bytes at voff go to LDS byte lds_wave_base + 16L.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
@@ -146,21 +142,11 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     const __amdgpu_buffer_rsrc_t rH =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
-    // ---- q8 tile: 32 dword LDS-direct loads per stage, 8 per wave. Load m of wave w
-    // covers LDS dwords 64(w + 4m) ..: tokens t = 2(w + 4m) + (lane >> 5), dword lane & 31
-    // of the row. The swizzle of token t is (w + 4m) & 7, so two per-lane patterns suffice.
-    int voQ[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-        const int sw = (wave + 4 * par) & 7, wd = lane & 31;
-        const int Gq = (wd >> 2) ^ sw, w4 = wd & 3;
-        voQ[par] = (2 * wave + (lane >> 5)) * K + 32 * (Gq >> 1) + perm_src(Gq, w4);
-    }
     // q8_1 header words of the stage: wave w brings chunk w of the stage, lane = token.
     const int voH = lane * nc * 4 + 4 * wave;
-    // Prepared path: the q8 tile in natural order by 16-byte loads, slab i = tokens
-    // 8i..8i+7 (8 lanes each), wave w slabs 2w, 2w+1; granule G of token t at slot
-    // G ^ aq_sw(t). Weights: the stage image, 16 slabs of 1 KiB, wave w slabs 4w..4w+3.
+    // The q8 tile in natural order by 16-byte loads, slab i = tokens 8i..8i+7 (8 lanes
+    // each), wave w slabs 2w, 2w+1; granule G of token t at slot G ^ aq_sw(t). Prepared
+    // weights: the stage image, 16 slabs of 1 KiB, wave w slabs 4w..4w+3.
     int voQ16[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -169,17 +155,12 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
     }
     auto issue_q8 = [&](int sb, int hh, StageLds& st) {
         const int off = sb * QK_K + hh * HALF;
-        if constexpr (PREP) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ16[i] + off);
+        for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ16[i] + off);
+        if constexpr (PREP)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 lds_load16(rW, st.bl + 1024 * (4 * wave + i), (sb * 2 + hh) * PREP_STAGE + 1024 * (4 * wave + i) + 16 * lane);
-        } else {
-#pragma unroll
-            for (int m = 0; m < 8; ++m)
-                lds_load4(rQ, st.aq + 256 * (wave + 4 * m), voQ[m & 1] + 8 * m * K + off);
-        }
         if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
     };
 
@@ -284,18 +265,10 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
 #pragma unroll
             for (int ts = 0; ts < 2; ++ts) {
                 __builtin_amdgcn_sched_barrier(0);
-                long b0, b1;
-                if constexpr (PREP) {
-                    // natural order: piece hg in granule 2cl, piece 2+hg in granule 2cl+1
-                    const uint8_t* row = st.aq + 128 * (32 * ts + l32) + 8 * hg;
-                    b0 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl) ^ tsw));
-                    b1 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl + 1) ^ tsw));
-                } else {
-                    const uint32x4 bq = *reinterpret_cast<const uint32x4*>(st.aq + 128 * (32 * ts + l32) +
-                                                                            16 * ((2 * cl + hg) ^ tsw));
-                    b0 = (long)(((unsigned long)bq[1] << 32) | bq[0]);
-                    b1 = (long)(((unsigned long)bq[3] << 32) | bq[2]);
-                }
+                // natural order: piece hg in granule 2cl, piece 2+hg in granule 2cl+1
+                const uint8_t* row = st.aq + 128 * (32 * ts + l32) + 8 * hg;
+                const long b0 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl) ^ tsw));
+                const long b1 = *reinterpret_cast<const long*>(row + 16 * ((2 * cl + 1) ^ tsw));
                 const int32x16 F0 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a0, b0, magic, 0, 0, 0);
                 const int32x16 F1 = __builtin_amdgcn_mfma_i32_32x32x16_i8(a1, b1, magic, 0, 0, 0);
                 if constexpr (ISUMS) {
