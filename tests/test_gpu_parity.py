@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from oracle import oracle as O
-from qblocks import tolerance_ok, encode_q4K
+from qblocks import tolerance_ok, encode_q4K, encode_q6K
 from quantized_prefill_gemm_amd import binding as B
 from quantized_prefill_gemm_amd import inputs
 
@@ -321,3 +321,42 @@ def test_calib_mfma_peak_runs():
     torch.cuda.synchronize()
     v = out.view(256, 4).cpu().numpy()
     assert (v[:, 0] > 0).all() and (v[:, 1] > 0).all() and (v[:, 3] == 0).all()
+
+
+def test_extreme_magnitudes():
+    """Integer sums at their largest magnitudes (|I| = 15*127*32 for q4_K, |J| = 32*127*16
+    for q6_K, the range the 1.5*2^23 accumulator constant has to hold): every nibble 15 /
+    every q6 value -32 or +31, extreme scales, activations of +-1 (q = +-127)."""
+    say("[extreme magnitudes]")
+    K = 512
+    X = np.ones((70, K), np.float32)
+    X[35:] = -1.0
+    X[69, ::2] = -1.0                                # mixed signs in one token
+    w4 = []
+    for j in range(130):
+        if j % 3 == 0:
+            w4.append(encode_q4K(0.5, 0.25, [63] * 8, [63] * 8, [15] * 256))
+        elif j % 3 == 1:
+            w4.append(encode_q4K(0.5, 0.0, [63] * 8, [0] * 8, [15 if e % 2 else 0 for e in range(256)]))
+        else:
+            w4.append(encode_q4K(0.5, 0.25, [0] * 8, [63] * 8, [0] * 256))
+    W4 = np.stack([np.concatenate([b] * (K // 256)) for b in w4])
+    w6 = []
+    for j in range(130):
+        if j % 2 == 0:
+            w6.append(encode_q6K(0.5, [-128] * 16, [-32] * 256))
+        else:
+            w6.append(encode_q6K(0.5, [127] * 16, [31] * 256))
+    W6 = np.stack([np.concatenate([b] * (K // 256)) for b in w6])
+    xq, (q, _, _) = gpu_quantize(X)
+    for wtype, W in (("q4_K", W4), ("q6_K", W6)):
+        M, N = X.shape[0], W.shape[0]
+        s = gpu_isums(wtype, W, xq, M, N, K)
+        ref = O.isums(wtype, W, q)
+        assert int(np.max(np.abs(ref))) == (15 * 127 * 32 if wtype == "q4_K" else 32 * 127 * 16)
+        assert np.array_equal(s, ref), wtype
+        check_out(gpu_mmq(wtype, W, X, N), O.mmq(wtype, W, X), f"extreme {wtype}")
+    wp = B.q6K_prepare(dev(W6.reshape(-1)), 130, K)
+    y = B.mmq_q6K_prep_q8(wp, xq, 70, 130, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq("q6_K", W6, X), "extreme q6_K prepared")
