@@ -132,6 +132,20 @@ def isums(wtype: str, w: np.ndarray, q: np.ndarray, nthreads: int | None = None)
     return s
 
 
+def q6K_chunk_sums(w: np.ndarray, q: np.ndarray, nthreads: int | None = None) -> np.ndarray:
+    """Scale-weighted integer sums of q6_K per 32-wide chunk: int32 [M, N, K/32] with
+    C[i, j, c] = sum over k in chunk c of sc[j, k/16] * v[j, k] * q[i, k] — the two 16-wide
+    sub-block sums J of the chunk, each times its int8 scale (the fold of q6_K without the
+    f32 factors da and d). |C| <= 2 * 128 * 16 * 32 * 127 < 2^31."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    J = isums("q6_K", w, q, nthreads).astype(np.int64)           # [M, N, K/16]
+    N, K = w.shape[0], q.shape[1]
+    nsb = K // 256
+    sc = w.reshape(N, nsb, 210)[:, :, 192:208].view(np.int8).astype(np.int64).reshape(N, K // 16)
+    C = J[:, :, 0::2] * sc[None, :, 0::2] + J[:, :, 1::2] * sc[None, :, 1::2]
+    return C.astype(np.int32)
+
+
 def mmq_q8(wtype: str, w: np.ndarray, q: np.ndarray, dh: np.ndarray, ss: np.ndarray,
            nthreads: int | None = None) -> np.ndarray:
     """fp64 [M, N] = fold of the exact integer sums (q8_1 activations given)."""

@@ -229,6 +229,40 @@ def test_q6K_signed_scale_sweep():
         assert y[u, 0] == 0.5 * sc[u] * 31 * DA127
 
 
+def test_q6K_chunk_sums_one_hot_and_closed_form():
+    """Scale-weighted chunk sums from encoder-chosen fields: a one-hot activation at k gives
+    sc[k/16] * v[k] * 127 in chunk k/32 and zero elsewhere; constant blocks give the closed
+    form 32 * 127 * sc * v; and the chunk sums fold to the oracle's output."""
+    rng = np.random.default_rng(23)
+    N, K = 5, 512
+    sc = rng.integers(-128, 128, (N, K // 16))
+    v = rng.integers(-32, 32, (N, K))
+    w = np.stack([np.concatenate([encode_q6K(0.25, sc[j, 16 * b:16 * b + 16], v[j, 256 * b:256 * b + 256])
+                                  for b in range(K // 256)]) for j in range(N)])
+    q, _, _ = O.quantize_q8_1(np.eye(K, dtype=np.float32))      # q = 127 on the diagonal
+    C = O.q6K_chunk_sums(w, q, nthreads=2)
+    assert C.shape == (K, N, K // 32)
+    for k in range(K):
+        want = np.zeros((N, K // 32), np.int64)
+        want[:, k // 32] = sc[:, k // 16] * v[:, k] * 127
+        assert np.array_equal(C[k], want), k
+    wc = np.stack([np.concatenate([encode_q6K(1.0, [-128] * 16, [-32] * 256)] * 2),
+                   np.concatenate([encode_q6K(1.0, [127] * 16, [31] * 256)] * 2)])
+    qc, dh, ss = O.quantize_q8_1(np.ones((3, K), np.float32))
+    Cc = O.q6K_chunk_sums(wc, qc, nthreads=1)
+    assert np.all(Cc[:, 0] == 32 * 127 * 128 * 32) and np.all(Cc[:, 1] == 32 * 127 * 127 * 31)
+    # folding the chunk sums with da and d reproduces the oracle's q6_K output
+    W, X = inputs.small_case("q6_K", 9, 7, 768, seed=4, gain=True)
+    q, dh, ss = O.quantize_q8_1(X)
+    C = O.q6K_chunk_sums(W, q, nthreads=2).astype(np.float64)
+    da = np.vectorize(O.f16_to_f64, otypes=[np.float64])(dh)                    # [M, K/32]
+    d = np.array([[O.decode_q6K(W[j, 210 * b:210 * b + 210])[0] for b in range(768 // 256)]
+                  for j in range(7)])                                           # [N, K/256]
+    y = np.einsum("ic,jc,ijc->ij", da, np.repeat(d, 8, axis=1), C)
+    r = O.mmq("q6_K", W, X, nthreads=2)
+    assert np.allclose(y, r, rtol=1e-12, atol=1e-9 * np.abs(r).max())
+
+
 # ----------------------------------------------------------------------------- brute force
 
 @pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
