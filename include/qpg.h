@@ -139,6 +139,34 @@ int mmq_q6K_prep_q8(const void* wp, const void* xq, float* y, int64_t M, int64_t
 int mmq_q6K_prep_isums(const void* wp, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
                        qpg_stream_t stream);
 
+/*
+ * Expanded q6_K weights: a one-time pass that applies each weight's int8 sub-block scale
+ * in the integer domain. The q6_K sum of "r40 - __launch_bounds__(256,3) third resident
+ * block" (sec. 5) has two 16-wide products per 32-wide q8_1 chunk, each with its own scale
+ * sc[u]; sum_u sc[u] * J_u is the same exact integer as sum_k (sc[k/16] * (q6_k - 32)) * q_k,
+ * so q6K_expand stores a = sc * (q6 - 32) (in [-4064, 4096]) per weight as two int8 digits
+ * (a = 64 * hi + lo) and the kernel forms the chunk sum with two K = 32 int8 products and a
+ * three-operation fold. q6K_expand reads raw q6_K blocks w [N][K/256] (any alignment) and
+ * writes we (qpg_q6K_exp_bytes(N, K) bytes = ceil(N/64) * (K/256) * 33,024, 16-byte aligned,
+ * caller-owned; 2.02 bytes per weight against 0.82 for the raw blocks): per 64-row tile and
+ * super-block the two digit planes of both half super-blocks and d as f32. The layout is
+ * library-internal: we is only meaningful to the _exp entry points of the same library and
+ * must be expanded again after w changes. Rows past N are zero-filled.
+ * mmq_q6K_exp_q8 computes what mmq_q6K_q8 computes (same tolerance against the exact
+ * result). mmq_q6K_exp_csums writes the exact integer chunk sums
+ * s[M][N][K/32] (int32, row-major, caller-owned): s[i][j][c] = sum over k in chunk c of
+ * sc[j][k/16] * (q6[j][k] - 32) * q[i][k] -- bit-exact, the witness of the integer stage.
+ * qpg_q6K_exp_bytes returns 0 for an unsupported shape (N < 1, K % 256 != 0,
+ * K > 2^24 - 256). Alignment: we, xq 16 bytes; y, s 4 bytes. Errors as above; nothing is
+ * allocated.
+ */
+size_t qpg_q6K_exp_bytes(int64_t N, int64_t K);
+int q6K_expand(const void* w, void* we, int64_t N, int64_t K, qpg_stream_t stream);
+int mmq_q6K_exp_q8(const void* we, const void* xq, float* y, int64_t M, int64_t N, int64_t K,
+                   qpg_stream_t stream);
+int mmq_q6K_exp_csums(const void* we, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                      qpg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -48,8 +48,14 @@ def lib() -> ctypes.CDLL:
         L.q6K_prepare.argtypes = [P, P, I64, I64, P]
         for f in (L.mmq_q6K_prep_q8, L.mmq_q6K_prep_isums):
             f.argtypes = [P, P, P, I64, I64, I64, P]
+        L.qpg_q6K_exp_bytes.argtypes = [I64, I64]
+        L.qpg_q6K_exp_bytes.restype = ctypes.c_size_t
+        L.q6K_expand.argtypes = [P, P, I64, I64, P]
+        for f in (L.mmq_q6K_exp_q8, L.mmq_q6K_exp_csums):
+            f.argtypes = [P, P, P, I64, I64, I64, P]
         for f in (L.quantize_q8_1, L.mmq_q4K, L.mmq_q6K, L.mmq_q4K_q8, L.mmq_q6K_q8, L.mmq_q4K_isums,
-                  L.mmq_q6K_isums, L.q6K_prepare, L.mmq_q6K_prep_q8, L.mmq_q6K_prep_isums):
+                  L.mmq_q6K_isums, L.q6K_prepare, L.mmq_q6K_prep_q8, L.mmq_q6K_prep_isums, L.q6K_expand,
+                  L.mmq_q6K_exp_q8, L.mmq_q6K_exp_csums):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -57,7 +63,8 @@ def lib() -> ctypes.CDLL:
 
 EXPORTS = ("qpg_strerror", "qpg_q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8",
            "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums", "qpg_q6K_prep_bytes", "q6K_prepare",
-           "mmq_q6K_prep_q8", "mmq_q6K_prep_isums")
+           "mmq_q6K_prep_q8", "mmq_q6K_prep_isums", "qpg_q6K_exp_bytes", "q6K_expand", "mmq_q6K_exp_q8",
+           "mmq_q6K_exp_csums")
 
 
 def _check(rc: int, what: str):
@@ -217,3 +224,52 @@ def mmq_q6K_prep_q8(wp, xq, M, N, K, y=None, stream=None):
 
 def mmq_q6K_prep_isums(wp, xq, M, N, K, s=None, stream=None):
     return _mmq_prep(wp, xq, M, N, K, s, stream, True)
+
+
+def q6K_exp_bytes(N: int, K: int) -> int:
+    return int(lib().qpg_q6K_exp_bytes(N, K))
+
+
+def q6K_expand(w: torch.Tensor, N: int, K: int, we=None, stream=None) -> torch.Tensor:
+    """Raw q6_K blocks (uint8, N*(K/256)*210 bytes, device) -> expanded layout (uint8)."""
+    _wcheck(w, N, K, 210)
+    nbytes = q6K_exp_bytes(N, K)
+    if nbytes == 0:
+        raise QPGError(QPG_EINVAL, f"unsupported shape N={N} K={K}")
+    if we is None:
+        we = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    _dev(we, torch.uint8, "we")
+    if we.numel() < nbytes:
+        raise QPGError(QPG_EINVAL, "we too small")
+    _check(lib().q6K_expand(_ptr(w), _ptr(we), N, K, _stream(stream)), "q6K_expand")
+    return we
+
+
+def _mmq_exp(we, xq, M, N, K, out, stream, csums: bool):
+    _dev(xq, torch.uint8, "xq")
+    if xq.numel() < q8_1_bytes(M, K):
+        raise QPGError(QPG_EINVAL, "xq too small")
+    _dev(we, torch.uint8, "we")
+    if we.numel() < q6K_exp_bytes(N, K):
+        raise QPGError(QPG_EINVAL, "we too small")
+    if csums:
+        if out is None:
+            out = torch.empty((M, N, K // 32), dtype=torch.int32, device=xq.device)
+        _dev(out, torch.int32, "s")
+        fn = lib().mmq_q6K_exp_csums
+    else:
+        if out is None:
+            out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+        _dev(out, torch.float32, "y")
+        fn = lib().mmq_q6K_exp_q8
+    _check(fn(_ptr(we), _ptr(xq), _ptr(out), M, N, K, _stream(stream)),
+           "mmq_q6K_exp_csums" if csums else "mmq_q6K_exp_q8")
+    return out
+
+
+def mmq_q6K_exp_q8(we, xq, M, N, K, y=None, stream=None):
+    return _mmq_exp(we, xq, M, N, K, y, stream, False)
+
+
+def mmq_q6K_exp_csums(we, xq, M, N, K, s=None, stream=None):
+    return _mmq_exp(we, xq, M, N, K, s, stream, True)

@@ -100,9 +100,62 @@ int mmq_prep_checked(const void* wp, const void* xq, float* y, int32_t* s, int64
     return status_of(qpg_launch_mmq_q6K_prep(wp, xq, y, s, M, N, K, st));
 }
 
+// Expanded q6_K: the per-tile record range (nsb * 33,024 bytes) must stay below 2^31.
+constexpr int64_t kExpTile = 64, kExpSb = 33024;
+
+int exp_shape_ok(int64_t N, int64_t K)
+{
+    return N >= 1 && N < kMaxDim && K >= 256 && K % 256 == 0 && K <= kMaxK && (K / 256) * kExpSb < kMaxDim &&
+           ((N + kExpTile - 1) / kExpTile) * (K / 256) < kMaxDim;
+}
+
+int mmq_exp_checked(const void* we, const void* xq, float* y, int32_t* s, int64_t M, int64_t N, int64_t K,
+                    hipStream_t st)
+{
+    if (!we || !xq || (!y && !s)) return QPG_EINVAL;
+    int rc = check_mmq_shape(M, N, K);
+    if (rc != QPG_OK) return rc;
+    if (!exp_shape_ok(N, K)) return QPG_EINVAL;
+    if (((M + 63) / 64) * ((N + kExpTile - 1) / kExpTile) >= kMaxDim) return QPG_EINVAL;
+    if (s && M * N * (K / 32) >= ((int64_t)1 << 40)) return QPG_EINVAL;
+    if (!aligned(we, 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4))) return QPG_EALIGN;
+    rc = check_device();
+    if (rc != QPG_OK) return rc;
+    return status_of(qpg_launch_mmq_q6K_exp(we, xq, y, s, M, N, K, st));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t qpg_q6K_exp_bytes(int64_t N, int64_t K)
+{
+    if (!exp_shape_ok(N, K)) return 0;
+    return (size_t)(((N + kExpTile - 1) / kExpTile) * (K / 256) * kExpSb);
+}
+
+int q6K_expand(const void* w, void* we, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!w || !we) return QPG_EINVAL;
+    if (!exp_shape_ok(N, K)) return QPG_EINVAL;
+    if (!aligned(we, 16)) return QPG_EALIGN;
+    const int rc = check_device();
+    if (rc != QPG_OK) return rc;
+    return status_of(qpg_launch_q6K_expand(w, we, N, K, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int mmq_q6K_exp_q8(const void* we, const void* xq, float* y, int64_t M, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!y) return QPG_EINVAL;
+    return mmq_exp_checked(we, xq, y, nullptr, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_exp_csums(const void* we, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
+                      qpg_stream_t stream)
+{
+    if (!s) return QPG_EINVAL;
+    return mmq_exp_checked(we, xq, nullptr, s, M, N, K, reinterpret_cast<hipStream_t>(stream));
+}
 
 size_t qpg_q6K_prep_bytes(int64_t N, int64_t K)
 {

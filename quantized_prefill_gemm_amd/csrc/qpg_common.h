@@ -59,3 +59,7 @@ hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* 
 hipError_t qpg_launch_q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int32_t* isums,
                                    int64_t M, int64_t N, int64_t K, hipStream_t s);
+// q6_K expanded layout: ceil(N/64) * (K/256) * 33,024 bytes (layout in mmq_q6k_exp.hip)
+hipError_t qpg_launch_q6K_expand(const void* w, void* we, int64_t N, int64_t K, hipStream_t s);
+hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int32_t* csums,
+                                  int64_t M, int64_t N, int64_t K, hipStream_t s);

@@ -41,6 +41,11 @@ def L():
     lib.qpg_q6K_prep_bytes.restype = ctypes.c_size_t
     lib.qpg_q6K_prep_bytes.argtypes = [I64, I64]
     lib.q6K_prepare.argtypes = [P, P, I64, I64, P]
+    lib.qpg_q6K_exp_bytes.restype = ctypes.c_size_t
+    lib.qpg_q6K_exp_bytes.argtypes = [I64, I64]
+    lib.q6K_expand.argtypes = [P, P, I64, I64, P]
+    for f in (lib.mmq_q6K_exp_q8, lib.mmq_q6K_exp_csums):
+        f.argtypes = [P, P, P, I64, I64, I64, P]
     return lib
 
 
@@ -90,7 +95,7 @@ def test_quantize_rejects(L, args, expect):
 
 
 @pytest.mark.parametrize("fn", ["mmq_q4K_q8", "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums", "mmq_q6K_prep_q8",
-                                "mmq_q6K_prep_isums"])
+                                "mmq_q6K_prep_isums", "mmq_q6K_exp_q8", "mmq_q6K_exp_csums"])
 @pytest.mark.parametrize("args,expect", [
     ((None, A16, A16, 64, 256, 256), EINVAL),
     ((A16, None, A16, 64, 256, 256), EINVAL),
@@ -132,6 +137,23 @@ def test_q6K_prepare_sizes_and_rejects(L):
     assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 1 << 24, None) == EINVAL
 
 
+def test_q6K_expand_sizes_and_rejects(L):
+    # 33,024 bytes per (64-row tile, super-block): two 16 KiB digit images and d per row
+    assert L.qpg_q6K_exp_bytes(4096, 11008) == 64 * 43 * 33024
+    assert L.qpg_q6K_exp_bytes(65, 256) == 2 * 1 * 33024
+    assert L.qpg_q6K_exp_bytes(1, 512) == 2 * 33024
+    for n, k in ((0, 256), (64, 0), (64, 300), (64, 128), (1 << 31, 256), (64, 1 << 24)):
+        assert L.qpg_q6K_exp_bytes(n, k) == 0
+    assert L.q6K_expand(None, A16, 64, 256, None) == EINVAL
+    assert L.q6K_expand(A16, None, 64, 256, None) == EINVAL
+    assert L.q6K_expand(A16, A16, 0, 256, None) == EINVAL
+    assert L.q6K_expand(A16, A16, 64, 288, None) == EINVAL
+    assert L.q6K_expand(A16, A8, 64, 256, None) == EALIGN      # expanded layout needs 16
+    assert L.mmq_q6K_exp_q8(A8, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K_exp_q8(A16, A16, A16, 64, 256, 1 << 24, None) == EINVAL
+    assert L.mmq_q6K_exp_csums(A16, A16, A2, 64, 256, 256, None) == EALIGN
+
+
 def _has_gpu():
     try:
         import torch
@@ -148,6 +170,8 @@ def test_valid_call_without_device_reports_edevice(L):
     assert L.quantize_q8_1(A16, A16, 64, 256, None) == EDEVICE
     assert L.q6K_prepare(A16, A16, 128, 256, None) == EDEVICE
     assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
+    assert L.q6K_expand(A2, A16, 64, 256, None) == EDEVICE          # raw blocks: any alignment
+    assert L.mmq_q6K_exp_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
 
 
 CALIB = os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so")

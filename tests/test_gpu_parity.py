@@ -235,6 +235,50 @@ def test_q6K_prep_config4_full():
     assert np.array_equal(s.cpu().numpy(), gpu_isums(wtype, Wr, xq, M, 256, K))
 
 
+# ----------------------------------------------------------------------------- expanded q6_K
+
+def gpu_expand(W, N, K):
+    we = B.q6K_expand(dev(W.reshape(-1)), N, K)
+    torch.cuda.synchronize()
+    return we
+
+
+@pytest.mark.parametrize("M,N,K", ISUM_SHAPES)
+def test_q6K_exp_csums_bitexact(M, N, K):
+    say(f"[q6_K expanded csums {M}x{N}x{K}]")
+    W, X = inputs.small_case("q6_K", M, N, K, seed=3)
+    xq, (q, _, _) = gpu_quantize(X)
+    s = B.mmq_q6K_exp_csums(gpu_expand(W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    ref = O.q6K_chunk_sums(W, q)
+    got = s.cpu().numpy()
+    assert np.array_equal(got, ref), f"mismatches: {np.count_nonzero(got != ref)}"
+
+
+@pytest.mark.parametrize("M,N,K", TAIL_SHAPES)
+def test_q6K_exp_tails(M, N, K):
+    say(f"[q6_K expanded mmq {M}x{N}x{K}]")
+    W, X = inputs.small_case("q6_K", M, N, K, seed=5, gain=True)
+    xq, _ = gpu_quantize(X)
+    y = B.mmq_q6K_exp_q8(gpu_expand(W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq("q6_K", W, X), f"exp {M}x{N}x{K}")
+
+
+def test_q6K_exp_config4_full():
+    wtype, M, N, K, W, X = inputs.make_config(4)
+    say(f"[q6_K expanded cfg4 {M}x{N}x{K}]")
+    xq, (q, _, _) = gpu_quantize(X)
+    y = B.mmq_q6K_exp_q8(gpu_expand(W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq(wtype, W, X), "exp cfg4")
+    rows = slice(0, 192)
+    Wr = np.ascontiguousarray(W[rows])
+    s = B.mmq_q6K_exp_csums(gpu_expand(Wr, 192, K), xq, M, 192, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), O.q6K_chunk_sums(Wr, q))
+
+
 def test_closed_form_scale_path_on_gpu():
     """All nib = 1, sc = 1, d = 1, X = 1: Y = K * 0.99993896484375 exactly (golden)."""
     K = 1024
@@ -259,11 +303,11 @@ def test_stack_sampled_rows():
 
 
 def test_graph_replay_matches_eager():
-    """A small two-layer stack (quantize + q4_K / q6_K / prepared q6_K GEMMs) captured as one
+    """A small two-layer stack (quantize + q4_K / q6_K / prepared / expanded q6_K GEMMs) captured as one
     graph: every replay, with eager work and synchronisations between replays, must give
     the eager outputs bit for bit."""
     M = 96
-    specs = [("q4_K", 384, 512), ("q6_K", 256, 768), ("q6p", 200, 1024), ("q4_K", 130, 768)]
+    specs = [("q4_K", 384, 512), ("q6_K", 256, 768), ("q6p", 200, 1024), ("q4_K", 130, 768), ("q6x", 190, 768)]
     mats, xs, xqs, ys = [], [], [], []
     for i, (kind, N, K) in enumerate(specs):
         wtype = "q4_K" if kind == "q4_K" else "q6_K"
@@ -271,6 +315,8 @@ def test_graph_replay_matches_eager():
         w = dev(W.reshape(-1))
         if kind == "q6p":
             w = B.q6K_prepare(w, N, K)
+        elif kind == "q6x":
+            w = B.q6K_expand(w, N, K)
         mats.append((kind, N, K, w))
         xs.append(dev(X))
         xqs.append(torch.empty(B.q8_1_bytes(M, K), dtype=torch.uint8, device=DEV))
@@ -283,8 +329,10 @@ def test_graph_replay_matches_eager():
                 B.mmq_q4K_q8(w, xq, M, N, K, y)
             elif kind == "q6_K":
                 B.mmq_q6K_q8(w, xq, M, N, K, y)
-            else:
+            elif kind == "q6p":
                 B.mmq_q6K_prep_q8(w, xq, M, N, K, y)
+            else:
+                B.mmq_q6K_exp_q8(w, xq, M, N, K, y)
 
     say("[graph replay]")
     run()
@@ -360,3 +408,12 @@ def test_extreme_magnitudes():
     y = B.mmq_q6K_prep_q8(wp, xq, 70, 130, K)
     torch.cuda.synchronize()
     check_out(y.cpu().numpy(), O.mmq("q6_K", W6, X), "extreme q6_K prepared")
+    # expanded: a = sc * (q6 - 32) reaches -4064 and 4096, the ends of its digit range
+    we = B.q6K_expand(dev(W6.reshape(-1)), 130, K)
+    s = B.mmq_q6K_exp_csums(we, xq, 70, 130, K)
+    y = B.mmq_q6K_exp_q8(we, xq, 70, 130, K)
+    torch.cuda.synchronize()
+    ref = O.q6K_chunk_sums(W6, q)
+    assert int(np.max(np.abs(ref))) == 32 * 127 * 128 * 32
+    assert np.array_equal(s.cpu().numpy(), ref)
+    check_out(y.cpu().numpy(), O.mmq("q6_K", W6, X), "extreme q6_K expanded")
