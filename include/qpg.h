@@ -147,8 +147,8 @@ int mmq_q6K_prep_isums(const void* wp, const void* xq, int32_t* s, int64_t M, in
  * so q6K_expand stores a = sc * (q6 - 32) (in [-4064, 4096]) per weight as two int8 digits
  * (a = 64 * hi + lo) and the kernel forms the chunk sum with two K = 32 int8 products and a
  * three-operation fold. q6K_expand reads raw q6_K blocks w [N][K/256] (any alignment) and
- * writes we (qpg_q6K_exp_bytes(N, K) bytes = ceil(N/64) * (K/256) * 33,024, 16-byte aligned,
- * caller-owned; 2.02 bytes per weight against 0.82 for the raw blocks): per 64-row tile and
+ * writes we (qpg_q6K_exp_bytes(N, K) bytes = ceil(N/64) * (K/256) * 35,072, 16-byte aligned,
+ * caller-owned; 2.14 bytes per weight against 0.82 for the raw blocks): per 64-row tile and
  * super-block the two digit planes of both half super-blocks and d as f32. The layout is
  * library-internal: we is only meaningful to the _exp entry points of the same library and
  * must be expanded again after w changes. Rows past N are zero-filled.

@@ -100,8 +100,8 @@ int mmq_prep_checked(const void* wp, const void* xq, float* y, int32_t* s, int64
     return status_of(qpg_launch_mmq_q6K_prep(wp, xq, y, s, M, N, K, st));
 }
 
-// Expanded q6_K: the per-tile record range (nsb * 33,024 bytes) must stay below 2^31.
-constexpr int64_t kExpTile = 64, kExpSb = 33024;
+// Expanded q6_K: the per-tile record range (nsb * 35,072 bytes) must stay below 2^31.
+constexpr int64_t kExpTile = 64, kExpSb = 35072;
 
 int exp_shape_ok(int64_t N, int64_t K)
 {

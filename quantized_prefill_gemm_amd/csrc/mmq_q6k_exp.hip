@@ -27,13 +27,14 @@
 //    value per lane, d is one value per register).
 //  * Two-deep pipeline of half super-blocks (128 k) with one barrier per stage, all of it
 //    moved by LDS-direct loads issued one stage ahead: the q8 tile (8 KiB, 16-byte loads,
-//    natural order), the digit image of the stage (16 KiB, a contiguous copy: the expand
+//    natural order), the digit image of the stage (17 KiB, a contiguous copy: the expand
 //    pass writes the exact LDS layout), the q8_1 header words (dword loads) and the
 //    super-block's d per row (256 B).
 //  * LDS layouts (per stage):
 //      aq: token t at 128 t, 16-byte granule G (k = 16G..16G+15) at slot G ^ ((t >> 1) & 7)
-//      ad: row j at 256 j, granule G = 4 cl + 2 p + hg (chunk cl, digit plane p = hi / lo,
-//          k-group hg) at slot G ^ (j & 15)
+//      ad: row j at 272 j (odd number of 16-byte slots: 16 rows read together hit 16
+//          different bank groups), granule G = 4 cl + 2 p + hg (chunk cl, digit plane
+//          p = hi / lo, k-group hg) at 16 G, so every read is one base plus an immediate
 //      d:  row j at 32 (j >> 5) + c_pos(j & 31), i.e. each lane's 16 rows contiguous.
 //  * When the matrix has at most 256 tiles (one per CU), three groups of four waves share a
 //    workgroup over contiguous super-block ranges and add their partial tiles in group
@@ -52,9 +53,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int TM = 64;
 constexpr int TN = 64;
 constexpr int HALF = 128;                       // k per pipeline stage
-constexpr int EXP_STAGE = TN * 256;             // digit image of one stage: 16 KiB
+constexpr int AD_PITCH = 272;                   // digit row: 16 granules + one pad granule
+constexpr int EXP_STAGE = TN * AD_PITCH;        // digit image of one stage: 17 KiB
 constexpr int EXP_D = TN * 4;                   // d per row of the super-block: 256 B
-constexpr int EXP_SB = 2 * EXP_STAGE + EXP_D;   // one (tile, super-block) record: 33,024 B
+constexpr int EXP_SB = 2 * EXP_STAGE + EXP_D;   // one (tile, super-block) record: 35,072 B
 
 struct StageLds {
     alignas(16) uint8_t aq[TM * HALF];
@@ -70,7 +72,6 @@ static_assert(3 * sizeof(GroupLds) <= 160 * 1024, "three groups per CU");
 static_assert(sizeof(GroupLds) >= TM * TN * 4, "a group's buffers hold its partial tile");
 
 __device__ __forceinline__ int aq_sw(int t) { return (t >> 1) & 7; }
-__device__ __forceinline__ int ad_sw(int j) { return j & 15; }
 // Position of row jj (0..31 of a 32-row half) in C-register order: lane half hg holds
 // registers r = 0..15 of rows 8(r>>2) + 4hg + (r&3) at 16 hg + r.
 __device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
@@ -132,8 +133,9 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
 
     // Per-lane source offsets. q8 tile: slab i = tokens 8i..8i+7 (8 lanes each), wave w
     // slabs 2w, 2w+1; lane L of slab i = token 8i + (L >> 3) at slot L & 7, which holds
-    // granule (L & 7) ^ aq_sw(t). Digits: 16 contiguous slabs of 1 KiB, wave w slabs
-    // 4w..4w+3. Header words: wave w brings chunk w of the stage, lane = token.
+    // granule (L & 7) ^ aq_sw(t). Digits: 17 contiguous slabs of 1 KiB, wave w slabs
+    // 4w..4w+3, wave 0 also slab 16. Header words: wave w brings chunk w of the stage,
+    // lane = token.
     int voQ[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -153,6 +155,7 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
         for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ[i]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) lds_load16(rW, st.ad + 1024 * (4 * wave + i), 1024 * (4 * wave + i) + 16 * lane);
+        if (wave == 0) lds_load16(rW, st.ad + 1024 * 16, 1024 * 16 + 16 * lane);     // 17th slab
         if constexpr (!CSUMS) {
             const unsigned oh = __builtin_amdgcn_readfirstlane((sb * 8 + 4 * hh) * 4);
             const __amdgpu_buffer_rsrc_t rH = __builtin_amdgcn_make_buffer_rsrc((void*)(hbase + oh), 0, (int)(nH - oh), 0x00020000);
@@ -173,18 +176,21 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
     for (int r = 0; r < 16; ++r) y[r] = 0.0f;
 
     const int jr = wr0 + l32, tt = wt0 + l32;       // A row and B token of this lane
-    const int asw = ad_sw(jr), bsw = aq_sw(tt);
+    // Lane offsets of the compute reads (the rest is immediates): A at row jr, k-group hg;
+    // B granule (2 cl + hg) ^ aq_sw(tt) of token tt for each chunk cl.
+    const int aoff = AD_PITCH * jr + 16 * hg;
+    int boff[4];
+#pragma unroll
+    for (int cl = 0; cl < 4; ++cl) boff[cl] = 128 * tt + 16 * ((2 * cl + hg) ^ aq_sw(tt));
 
     // Integer stage + fold over the four chunks of one stage, the two MFMAs of chunk cl+1
     // issued before the fold of chunk cl.
     auto compute_stage = [&](int sb, int hh, const StageLds& st) {
         if constexpr (!CSUMS) asm volatile("" : "+v"(magic));   // keep the constant in VGPRs
-        const uint8_t* arow = st.ad + 256 * jr;
-        const uint8_t* brow = st.aq + 128 * tt;
         auto ldA = [&](int cl, int p) -> int32x4 {
-            return *reinterpret_cast<const int32x4*>(arow + 16 * ((4 * cl + 2 * p + hg) ^ asw));
+            return *reinterpret_cast<const int32x4*>(st.ad + aoff + 16 * (4 * cl + 2 * p));
         };
-        auto ldB = [&](int cl) -> int32x4 { return *reinterpret_cast<const int32x4*>(brow + 16 * ((2 * cl + hg) ^ bsw)); };
+        auto ldB = [&](int cl) -> int32x4 { return *reinterpret_cast<const int32x4*>(st.aq + boff[cl]); };
         floatx4 dv[4];
         if constexpr (!CSUMS) {
             const floatx4* dp = reinterpret_cast<const floatx4*>(&st.d[wr0 + 16 * hg]);
@@ -242,14 +248,21 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
     // Every group runs the same number of stages so that all waves meet at every barrier.
     const int nbase = nsb / KS, nrem = nsb % KS;
     const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
-    const int nst = 2 * cnt, nst_all = 2 * (nbase + (nrem ? 1 : 0));
-    if (nst > 0) issue_stage(sb0, 0, G.st[0]);
-    for (int h = 0; h < nst_all; ++h) {
-        const int sb = sb0 + (h >> 1), hh = h & 1, cur = h & 1;
+    const int iters = nbase + (nrem ? 1 : 0);
+    // Stage (sb, 0) lives in buffer 0 and (sb, 1) in buffer 1, so every LDS address of the
+    // compute is a lane offset plus an immediate.
+    if (cnt > 0) issue_stage(sb0, 0, G.st[0]);
+    for (int it = 0; it < iters; ++it) {
+        const int sb = sb0 + it;
+        const bool act = it < cnt, more = it + 1 < cnt;
         wait_vmem();
-        __syncthreads();                    // stage h visible in buffer cur; buffer cur^1 free
-        if (h + 1 < nst) issue_stage(sb0 + ((h + 1) >> 1), (h + 1) & 1, G.st[cur ^ 1]);
-        if (h < nst) compute_stage(sb, hh, G.st[cur]);
+        __syncthreads();                    // stage (sb,0) visible in buffer 0; buffer 1 free
+        if (act) issue_stage(sb, 1, G.st[1]);
+        if (act) compute_stage(sb, 0, G.st[0]);
+        wait_vmem();
+        __syncthreads();                    // stage (sb,1) visible in buffer 1; buffer 0 free
+        if (more) issue_stage(sb + 1, 0, G.st[0]);
+        if (act) compute_stage(sb, 1, G.st[1]);
     }
 
     if constexpr (!CSUMS && KS > 1) {
@@ -333,17 +346,16 @@ __global__ void __launch_bounds__(256) q6K_expand_kernel(const uint8_t* __restri
         d = half_bits_to_float((uint32_t)blk[208] | ((uint32_t)blk[209] << 8));
     }
     uint8_t* rec = WE + ((size_t)T * nsb + sb) * EXP_SB;
-    uint8_t* row = rec + hh * EXP_STAGE + 256 * j;
+    uint8_t* row = rec + hh * EXP_STAGE + AD_PITCH * j;
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const int cl = 2 * (qq & 1) + x, q = 4 * (2 * x + g);       // dword index of the granule
-            *reinterpret_cast<uint32x4*>(row + 16 * ((4 * cl + 0 + g) ^ ad_sw(j))) =
-                uint32x4{hi[q], hi[q + 1], hi[q + 2], hi[q + 3]};
-            *reinterpret_cast<uint32x4*>(row + 16 * ((4 * cl + 2 + g) ^ ad_sw(j))) =
-                uint32x4{lo[q], lo[q + 1], lo[q + 2], lo[q + 3]};
+            *reinterpret_cast<uint32x4*>(row + 16 * (4 * cl + 0 + g)) = uint32x4{hi[q], hi[q + 1], hi[q + 2], hi[q + 3]};
+            *reinterpret_cast<uint32x4*>(row + 16 * (4 * cl + 2 + g)) = uint32x4{lo[q], lo[q + 1], lo[q + 2], lo[q + 3]};
         }
+    if ((qq & 1) == 0) *reinterpret_cast<uint32x4*>(row + 256) = uint32x4{0u, 0u, 0u, 0u};     // pad granule
     if (qq == 0) reinterpret_cast<float*>(rec + 2 * EXP_STAGE)[32 * (j >> 5) + c_pos(j & 31)] = d;
 }
 

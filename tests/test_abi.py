@@ -138,10 +138,10 @@ def test_q6K_prepare_sizes_and_rejects(L):
 
 
 def test_q6K_expand_sizes_and_rejects(L):
-    # 33,024 bytes per (64-row tile, super-block): two 16 KiB digit images and d per row
-    assert L.qpg_q6K_exp_bytes(4096, 11008) == 64 * 43 * 33024
-    assert L.qpg_q6K_exp_bytes(65, 256) == 2 * 1 * 33024
-    assert L.qpg_q6K_exp_bytes(1, 512) == 2 * 33024
+    # 35,072 bytes per (64-row tile, super-block): two 17 KiB digit images and d per row
+    assert L.qpg_q6K_exp_bytes(4096, 11008) == 64 * 43 * 35072
+    assert L.qpg_q6K_exp_bytes(65, 256) == 2 * 1 * 35072
+    assert L.qpg_q6K_exp_bytes(1, 512) == 2 * 35072
     for n, k in ((0, 256), (64, 0), (64, 300), (64, 128), (1 << 31, 256), (64, 1 << 24)):
         assert L.qpg_q6K_exp_bytes(n, k) == 0
     assert L.q6K_expand(None, A16, 64, 256, None) == EINVAL
