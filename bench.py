@@ -52,7 +52,8 @@ def load_traffic():
 
 
 def algorithmic_bytes(M, N, K, wbytes_per_block=144):
-    """Bytes the MMQ kernel must move at least once: weights, q8_1 activations, f32 output."""
+    """Bytes the MMQ kernel must move at least once: weights (bytes per row and 256 weights:
+    144 q4_K, 210 q6_K, 256 prepared q6_K, 548 expanded q6_K), q8_1 activations, f32 output."""
     return N * (K // 256) * wbytes_per_block + (M * K + 4 * M * (K // 32)) + 4 * M * N
 
 
@@ -70,13 +71,16 @@ def setup(cfg: int):
     return B, wtype, M, N, K, W, X, w, x, y, ws
 
 
-def run_gpu(cfg: int, steps: int, warmup: int, prepared: bool = False):
+def run_gpu(cfg: int, steps: int, warmup: int, q6: str = "raw"):
     import torch
     B, wtype, M, N, K, W, X, w, x, y, ws = setup(cfg)
     mmq_q8 = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
-    if prepared and wtype == "q6_K":
+    if q6 == "prepared" and wtype == "q6_K":
         w = B.q6K_prepare(w, N, K)          # one-time repack, outside the timed region
         mmq_q8 = B.mmq_q6K_prep_q8
+    elif q6 == "expanded" and wtype == "q6_K":
+        w = B.q6K_expand(w, N, K)           # one-time expansion, outside the timed region
+        mmq_q8 = B.mmq_q6K_exp_q8
     stream = torch.cuda.current_stream()
 
     def step():
@@ -156,7 +160,7 @@ def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
             "kernel": "v_mfma_i32_32x32x32_i8 chains, 2 waves per SIMD", "seconds": round(secs, 5)}
 
 
-def run_stack(steps: int, warmup: int, prepared: bool):
+def run_stack(steps: int, warmup: int, q6: str):
     """Config 5: the 32-layer 7B-shaped stack at M = 1024, each of the 7 GEMMs of a layer
     preceded by its quantize_q8_1: 448 launches per pass, timed both as one HIP graph (torch's
     graph API over the library's own launches) replayed, and launched eagerly. Weights: the seeded per-layer
@@ -172,8 +176,10 @@ def run_stack(steps: int, warmup: int, prepared: bool):
         for idx in range(len(inputs.STACK_LAYER)):
             name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
             w = torch.from_numpy(W.reshape(-1)).to(dev)
-            if wtype == "q6_K" and prepared:
+            if wtype == "q6_K" and q6 == "prepared":
                 w = B.q6K_prepare(w, N, K)
+            elif wtype == "q6_K" and q6 == "expanded":
+                w = B.q6K_expand(w, N, K)
             mats.append((idx, wtype, N, K, w))
         torch.cuda.synchronize()
         if layer % 8 == 7:
@@ -190,8 +196,10 @@ def run_stack(steps: int, warmup: int, prepared: bool):
     def mmq(idx, wtype, N, K, w, xq):
         if wtype == "q4_K":
             B.mmq_q4K_q8(w, xq, M, N, K, ys[idx])
-        elif prepared:
+        elif q6 == "prepared":
             B.mmq_q6K_prep_q8(w, xq, M, N, K, ys[idx])
+        elif q6 == "expanded":
+            B.mmq_q6K_exp_q8(w, xq, M, N, K, ys[idx])
         else:
             B.mmq_q6K_q8(w, xq, M, N, K, ys[idx])
 
@@ -306,10 +314,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=3,
                     help="workload 2/3 (q4_K), 4 (q6_K) or 5 (the 32-layer stack as one graph)")
-    ap.add_argument("--prepared", action="store_true",
-                    help="q6_K weights through the one-time prepare pass (config 4; always used for 5 "
-                         "unless --raw-q6k)")
-    ap.add_argument("--raw-q6k", action="store_true", help="config 5: q6_K GEMMs on raw blocks")
+    ap.add_argument("--q6k", choices=["raw", "prepared", "expanded"], default=None,
+                    help="q6_K weight form: raw blocks, the prepared repack or the expanded digits "
+                         "(made once, outside the timed region); default raw for config 4, expanded "
+                         "for config 5")
+    ap.add_argument("--prepared", action="store_true", help="same as --q6k prepared")
+    ap.add_argument("--expanded", action="store_true", help="same as --q6k expanded")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile", choices=["q4K", "q6K", "quant"])
     ap.add_argument("--launches", type=int, default=20)
@@ -329,7 +339,8 @@ def main():
     if a.config == 5:
         steps = a.steps if a.steps != ap.get_default("steps") else 10
         warmup = a.warmup if a.warmup != ap.get_default("warmup") else 2
-        macs, res = run_stack(steps, warmup, prepared=not a.raw_q6k)
+        q6 = a.q6k or ("prepared" if a.prepared else "expanded")
+        macs, res = run_stack(steps, warmup, q6)
         ms = res["all"]
         out = {
             "metric": METRIC, "value": round(macs / (ms * 1e-3) / 1e12, 3), "unit": "TMAC/s", "n_gpus": 1,
@@ -338,7 +349,8 @@ def main():
             "config": {"workload": "32-layer 7B-shaped stack, M=1024: q/k/o 4096x4096 q4_K, v 4096x4096 q6_K, "
                                    "gate/up 11008x4096 q4_K, down 4096x11008 q6_K, quantize_q8_1 before each "
                                    "GEMM; 448 launches per pass, as one HIP graph or eagerly, whichever is faster",
-                       "M": 1024, "layers": 32, "q6_K": "raw blocks" if a.raw_q6k else "prepared"},
+                       "M": 1024, "layers": 32, "q6_K": {"raw": "raw blocks", "prepared": "prepared",
+                                                         "expanded": "expanded digits"}[q6]},
             "stack_ms": {k: round(v, 4) for k, v in res.items()},
             "launch": "graph" if res["all_graph"] <= res["all_eager"] else "eager",
             "stack_tmacs": {"with_7_quantizes": round(macs / (res["all"] * 1e-3) / 1e12, 3),
@@ -350,7 +362,8 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
-    r = run_gpu(a.config, a.steps, a.warmup, prepared=a.prepared)
+    q6 = a.q6k or ("prepared" if a.prepared else "expanded" if a.expanded else "raw")
+    r = run_gpu(a.config, a.steps, a.warmup, q6=q6)
     M, N, K = r["M"], r["N"], r["K"]
     macs = M * N * K
     ms_step = r["step_ms"]
@@ -373,18 +386,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{r['wtype']} MMQ + q8_1 quantize, M={M} tokens x N={N} x K={K}"
                                + (" (FFN gate/up shape, per-token gains U[0.5,2])" if a.config == 3 else "")
-                               + (" (q6_K weights prepared once, outside the timed steps)"
-                                  if a.prepared and r["wtype"] == "q6_K" else ""),
+                               + ({"prepared": " (q6_K weights prepared once, outside the timed steps)",
+                                   "expanded": " (q6_K weights expanded once, outside the timed steps)"}
+                                  .get(q6, "") if r["wtype"] == "q6_K" else ""),
                    "M": M, "N": N, "K": K, "weights": r["wtype"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 5), "traffic": traffic,
-                     "kernel": f"mmq_{r['wtype'].replace('_', '')}_kernel", "avg_us": round(r["mmq_ms"] * 1e3, 3),
+                     "kernel": f"mmq_{r['wtype'].replace('_', '')}{'_exp' if q6 == 'expanded' and r['wtype'] == 'q6_K' else ''}_kernel",
+                     "avg_us": round(r["mmq_ms"] * 1e3, 3),
                      "note": "int8 ops counted as 2 per MAC, as in the 5.0 POP/s dense peak"},
         "kernels_us": {"quantize_q8_1": round(r["quant_ms"] * 1e3, 3), "mmq": round(r["mmq_ms"] * 1e3, 3),
                        "timing": "HIP events on the launch stream around K back-to-back launches of "
                                  "each kernel, right after the K timed steps"},
         "mmq_tmacs": round(macs / mmq_s / 1e12, 3),
-        "mmq_hbm_gbs_algorithmic": round(algorithmic_bytes(M, N, K, 144 if r["wtype"] == "q4_K" else 210)
+        "mmq_hbm_gbs_algorithmic": round(algorithmic_bytes(M, N, K, 144 if r["wtype"] == "q4_K" else
+                                                           {"raw": 210, "prepared": 256, "expanded": 548}[q6])
                                          / mmq_s / 1e9, 1),
         "wall_s": round(r["wall_s"], 4),
     }
