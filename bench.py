@@ -9,7 +9,8 @@ Prints ONE JSON line (metric, value in TMAC/s = M*N*K / step time, roofline of t
 kernel, CPU-oracle baseline). Defaults: 200 warm-up and 1000 timed steps (~100 ms of GPU
 time): the first ~10-20 ms of a run are up to 10 % slower while the clock ramps up.
 Other modes (for rocprofv3 runs):
-  --profile {q4K,q6K,quant}  a few launches of one kernel, no timing output
+  --profile {q4K,q6K,q6Kp,q6Kx,quant}  a few launches of one kernel (q6_K raw / prepared /
+                             expanded), no timing output
   --copy-calibration         a device-to-device copy of known size (HBM counter scale)
 """
 from __future__ import annotations
@@ -284,14 +285,17 @@ def stack_cpu_baseline():
 
 def profile_mode(which: str, launches: int):
     import torch
-    cfg = {"q4K": 3, "q6K": 4, "quant": 3}[which]
+    cfg = {"q4K": 3, "q6K": 4, "q6Kp": 4, "q6Kx": 4, "quant": 3}[which]
     B, wtype, M, N, K, W, X, w, x, y, ws = setup(cfg)
+    mmq = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
+    if which == "q6Kp":
+        w, mmq = B.q6K_prepare(w, N, K), B.mmq_q6K_prep_q8
+    elif which == "q6Kx":
+        w, mmq = B.q6K_expand(w, N, K), B.mmq_q6K_exp_q8
     for _ in range(launches):
-        if which == "quant":
-            B.quantize_q8_1(x, ws)
-        else:
-            B.quantize_q8_1(x, ws)
-            (B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8)(w, ws, M, N, K, y)
+        B.quantize_q8_1(x, ws)
+        if which != "quant":
+            mmq(w, ws, M, N, K, y)
     torch.cuda.synchronize()
     print(f"profiled {which}: {launches} launches of {wtype} {M}x{N}x{K}", flush=True)
 
@@ -321,7 +325,7 @@ def main():
     ap.add_argument("--prepared", action="store_true", help="same as --q6k prepared")
     ap.add_argument("--expanded", action="store_true", help="same as --q6k expanded")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile", choices=["q4K", "q6K", "quant"])
+    ap.add_argument("--profile", choices=["q4K", "q6K", "q6Kp", "q6Kx", "quant"])
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     a = ap.parse_args()

@@ -283,7 +283,10 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
                         }
                     }
                 } else {
-                    const float da = half_bits_to_float(st.hw[cl][32 * ts + l32] & 0xFFFFu);
+                    float da = half_bits_to_float(st.hw[cl][32 * ts + l32] & 0xFFFFu);
+                    // an f32 register, so the fold is v_fma_f32 (a mixed-precision v_fma_mix_f32
+                    // reading the f16 half directly issues at ~2/3 the rate)
+                    asm volatile("" : "+v"(da));
                     const float c0 = -MAGIC_F * da;                                       // exact
 #pragma unroll
                     for (int s = 0; s < 2; ++s) {

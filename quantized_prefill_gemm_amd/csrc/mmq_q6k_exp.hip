@@ -226,7 +226,10 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
                         S[((size_t)tok * N + row) * nc + sb * 8 + 4 * hh + cl] = 64 * (fh[r] - MAGIC_BITS) + (fl[r] - MAGIC_BITS);
                 }
             } else {
-                const float da = half_bits_to_float(st.hw[cl][tt] & 0xFFFFu);
+                float da = half_bits_to_float(st.hw[cl][tt] & 0xFFFFu);
+                // an f32 register, so that t2 is a v_fmac_f32 (reading the f16 half directly
+                // makes it a mixed-precision v_fma_mix_f32, which issues at ~2/3 the rate)
+                asm volatile("" : "+v"(da));
                 const float da64 = 64.0f * da, c1 = -65.0f * MAGIC_F * da;          // both exact
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4)
