@@ -22,9 +22,12 @@
 //    1.5*2^23*da, so its rounding (<= ~da) is the only error beyond the final f32 sums.
 //
 // MI355X design:
-//  * Tile 64 tokens x 64 weight rows per group of 4 waves: wave w owns the 32x32 sub-tile of
-//    rows 32*(w&1).. and tokens 32*(w>>1).. (weight rows on the MFMA row side: da is one
-//    value per lane, d is one value per register).
+//  * Tile 64 tokens x 64 weight rows: four 32x32 sub-tiles, rows 32*(w&1).. and tokens
+//    32*((w>>1)&1).. (weight rows on the MFMA row side: da is one value per lane, d one value
+//    per register). Eight waves per tile: waves w and w+4 compute the same sub-tile over
+//    chunks 0-1 and 2-3 of every stage and add their partial sums at the end, so two
+//    workgroups per CU give four waves per SIMD (121 VGPRs; one 32x32 tile per wave alone
+//    would leave two).
 //  * Two-deep pipeline of half super-blocks (128 k) with one barrier per stage, all of it
 //    moved by LDS-direct loads issued one stage ahead: the q8 tile (8 KiB, 16-byte loads,
 //    natural order), the digit image of the stage (17 KiB, a contiguous copy: the expand
@@ -105,20 +108,26 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_w
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
 }
 
-template <bool CSUMS, int KS>
-__global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_exp_kernel(
+// KS groups of 4 waves over contiguous super-block ranges (few tiles), or KW = 2: 8 waves
+// on one tile, waves w and w + 4 computing the same sub-tile over chunks 0-1 and 2-3 of each
+// stage (four waves per SIMD with two workgroups per CU).
+template <bool CSUMS, int KS, int KW>
+__global__ void __launch_bounds__(256 * KS * KW, (CSUMS || KS > 1) ? 1 : (KW > 1 ? 2 : 3)) mmq_q6K_exp_kernel(
     const uint8_t* __restrict__ WE, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
     float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total)
 {
+    static_assert(KS == 1 || KW == 1, "a K split over groups or over waves, not both");
+    constexpr int NW = 4 * KW;                      // waves sharing one set of stage buffers
     __shared__ GroupLds lds_all[KS];
     int m_tile, n_tile;
     tile_coords(m_tile, n_tile, tiles_m, total);
     const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
     GroupLds& G = lds_all[grp];
-    const int tid = threadIdx.x & 255, lane = tid & 63;
+    const int tid = threadIdx.x & (64 * NW - 1), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave >> 2;                       // chunk half of the stage (KW = 2)
     const int hg = lane >> 5, l32 = lane & 31;
-    const int wr0 = 32 * (wave & 1), wt0 = 32 * (wave >> 1);
+    const int wr0 = 32 * (wave & 1), wt0 = 32 * ((wave >> 1) & 1);
     const int m0 = m_tile * TM, n0 = n_tile * TN;
     const int nsb = K / QK_K, nc = K / QK8;
     const int rows_t = min(TM, M - m0);
@@ -136,13 +145,15 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
     // granule (L & 7) ^ aq_sw(t). Digits: 17 contiguous slabs of 1 KiB, wave w slabs
     // 4w..4w+3, wave 0 also slab 16. Header words: wave w brings chunk w of the stage,
     // lane = token.
-    int voQ[2];
+    // (With 8 waves each takes one q8 slab and two digit slabs.)
+    constexpr int QS = 8 / NW, DS = 16 / NW;        // q8 / digit slabs per wave
+    int voQ[QS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int t = 8 * (2 * wave + i) + (lane >> 3);
+    for (int i = 0; i < QS; ++i) {
+        const int t = 8 * (QS * wave + i) + (lane >> 3);
         voQ[i] = t * K + 16 * ((lane & 7) ^ aq_sw(t));
     }
-    const int voH = lane * nc * 4 + 4 * wave;
+    const int voH = lane * nc * 4 + 4 * (wave & 3);
 
     // The stage offset moves each descriptor's base (scalar arithmetic) and shrinks its
     // range by the same amount, so the per-lane offsets stay fixed and the bounds unchanged.
@@ -152,14 +163,14 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
         const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)(qbase + oq), 0, (int)(nQ - oq), 0x00020000);
         const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc((void*)(wtile + ow), 0, (int)(nW - ow), 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ[i]);
+        for (int i = 0; i < QS; ++i) lds_load16(rQ, st.aq + 1024 * (QS * wave + i), voQ[i]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_load16(rW, st.ad + 1024 * (4 * wave + i), 1024 * (4 * wave + i) + 16 * lane);
+        for (int i = 0; i < DS; ++i) lds_load16(rW, st.ad + 1024 * (DS * wave + i), 1024 * (DS * wave + i) + 16 * lane);
         if (wave == 0) lds_load16(rW, st.ad + 1024 * 16, 1024 * 16 + 16 * lane);     // 17th slab
         if constexpr (!CSUMS) {
             const unsigned oh = __builtin_amdgcn_readfirstlane((sb * 8 + 4 * hh) * 4);
             const __amdgpu_buffer_rsrc_t rH = __builtin_amdgcn_make_buffer_rsrc((void*)(hbase + oh), 0, (int)(nH - oh), 0x00020000);
-            lds_load4(rH, &st.hw[wave][0], voH);
+            if (wave < 4) lds_load4(rH, &st.hw[wave][0], voH);
             if (wave == 0 && lane < 16) {
                 const unsigned od = __builtin_amdgcn_readfirstlane(sb * EXP_SB + 2 * EXP_STAGE);
                 const __amdgpu_buffer_rsrc_t rD = __builtin_amdgcn_make_buffer_rsrc((void*)(wtile + od), 0, EXP_D, 0x00020000);
@@ -197,26 +208,7 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) dv[q4] = dp[q4];
         }
-        int32x16 FH[2], FL[2];
-        {
-            const int32x4 b = ldB(0);
-            FH[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(0, 0), b, magic, 0, 0, 0);
-            FL[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(0, 1), b, magic, 0, 0, 0);
-        }
-#pragma unroll
-        for (int cl = 0; cl < 4; ++cl) {
-            int32x4 bn, ahn, aln;
-            if (cl + 1 < 4) {
-                bn = ldB(cl + 1);
-                ahn = ldA(cl + 1, 0);
-                aln = ldA(cl + 1, 1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            if (cl + 1 < 4) {
-                FH[(cl + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahn, bn, magic, 0, 0, 0);
-                FL[(cl + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aln, bn, magic, 0, 0, 0);
-            }
-            const int32x16 fh = FH[cl & 1], fl = FL[cl & 1];
+        auto fold = [&](int cl, const int32x16& fh, const int32x16& fl) {
             if constexpr (CSUMS) {
                 const int tok = m0 + tt;
 #pragma unroll
@@ -241,7 +233,40 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
                         y[r] = fmaf(t2, dv[q4][e], y[r]);
                     }
             }
-            __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (KW > 1) {
+            // two chunks per wave; the other waves of the SIMD cover the MFMA latency
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int cl = 2 * kh + x;
+                const int32x4 b = ldB(cl);
+                const int32x16 fh = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(cl, 0), b, magic, 0, 0, 0);
+                const int32x16 fl = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(cl, 1), b, magic, 0, 0, 0);
+                fold(cl, fh, fl);
+            }
+        } else {
+            int32x16 FH[2], FL[2];
+            {
+                const int32x4 b = ldB(0);
+                FH[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(0, 0), b, magic, 0, 0, 0);
+                FL[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ldA(0, 1), b, magic, 0, 0, 0);
+            }
+#pragma unroll
+            for (int cl = 0; cl < 4; ++cl) {
+                int32x4 bn, ahn, aln;
+                if (cl + 1 < 4) {
+                    bn = ldB(cl + 1);
+                    ahn = ldA(cl + 1, 0);
+                    aln = ldA(cl + 1, 1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (cl + 1 < 4) {
+                    FH[(cl + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ahn, bn, magic, 0, 0, 0);
+                    FL[(cl + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aln, bn, magic, 0, 0, 0);
+                }
+                fold(cl, FH[cl & 1], FL[cl & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // folds of this stage done here (not sunk past the next barrier)
         asm volatile("" : "+v"(y));
@@ -288,6 +313,24 @@ __global__ void __launch_bounds__(256 * KS, (CSUMS || KS > 1) ? 1 : 3) mmq_q6K_e
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[4 * q + e] += p[e];
             }
+        }
+    }
+
+    if constexpr (!CSUMS && KW > 1) {
+        // waves 4..7 hand their chunk-half partial sums to waves 0..3, which add them (in
+        // that fixed order) and store; layout float4 q at (q * 256 + thread) * 16 bytes
+        __syncthreads();                    // every wave is done with the stage buffers
+        floatx4* red = reinterpret_cast<floatx4*>(&G);
+        if (kh == 1)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) red[q * 256 + (tid & 255)] = floatx4{y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]};
+        __syncthreads();
+        if (kh == 1) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const floatx4 p = red[q * 256 + tid];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[4 * q + e] += p[e];
         }
     }
 
@@ -384,21 +427,22 @@ hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int3
     const int8_t* qplane = static_cast<const int8_t*>(xq);
     const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
     const uint8_t* wb = static_cast<const uint8_t*>(we);
-    // At most one tile per CU: split each tile's super-blocks over three groups.
+    // At most one tile per CU: split each tile's super-blocks over three groups; otherwise
+    // eight waves per tile (two per SIMD) split each stage's chunks.
     const bool split = total <= 256 && K / 256 >= 3;
     if (csums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 3, 1>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
                                (int)M, (int)N, (int)K, tiles_m, total);
         else
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, csums,
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 1, 2>), dim3(total), dim3(512), 0, s, wb, qplane, hdr, y, csums,
                                (int)M, (int)N, (int)K, tiles_m, total);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 3, 1>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
                                (int)M, (int)N, (int)K, tiles_m, total);
         else
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, csums,
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 1, 2>), dim3(total), dim3(512), 0, s, wb, qplane, hdr, y, csums,
                                (int)M, (int)N, (int)K, tiles_m, total);
     }
     return hipGetLastError();
