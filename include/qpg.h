@@ -167,6 +167,32 @@ int mmq_q6K_exp_q8(const void* we, const void* xq, float* y, int64_t M, int64_t 
 int mmq_q6K_exp_csums(const void* we, const void* xq, int32_t* s, int64_t M, int64_t N, int64_t K,
                       qpg_stream_t stream);
 
+/*
+ * K split over workgroups, for shapes with few output tiles (a tensor-parallel shard, a
+ * short prompt against a narrow matrix): the same sums as the entry points without _sk
+ * (mmq_q4K_q8, mmq_q6K_q8, mmq_q6K_prep_q8, mmq_q6K_exp_q8; same operands, alignment and
+ * tolerance), with the super-block range of each output tile cut into P contiguous pieces
+ * that run as separate workgroups. Each piece writes its partial tile to plane p of the
+ * caller's workspace ws (f32 [P][M][N]); a second kernel then sums the planes in piece
+ * order into y, so the result is deterministic and independent of scheduling.
+ * qpg_mmq_sk_bytes(M, N, K, form) gives the workspace size in bytes (form 0 q4_K, 1 q6_K,
+ * 2 prepared q6_K, 3 expanded q6_K): P*M*N*4, or 0 when the shape needs no split
+ * (more than 128 tiles of 64 x 128, 64 x 64 for form 3, or fewer than 6 super-blocks)
+ * or is unsupported; with 0, ws may be null and the call is the plain entry point. P is
+ * at most 8, at most 256 / tiles and keeps >= 3 super-blocks per piece. ws must be 16-byte
+ * aligned and at least that large (QPG_EINVAL otherwise); it is caller-owned scratch whose
+ * contents are overwritten. Calls that share ws must not overlap in time.
+ */
+size_t qpg_mmq_sk_bytes(int64_t M, int64_t N, int64_t K, int form);
+int mmq_q4K_q8_sk(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                  size_t ws_bytes, qpg_stream_t stream);
+int mmq_q6K_q8_sk(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                  size_t ws_bytes, qpg_stream_t stream);
+int mmq_q6K_prep_q8_sk(const void* wp, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                       size_t ws_bytes, qpg_stream_t stream);
+int mmq_q6K_exp_q8_sk(const void* we, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                      size_t ws_bytes, qpg_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

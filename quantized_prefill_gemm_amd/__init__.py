@@ -9,7 +9,7 @@ from . import inputs  # noqa: F401  (seeded synthetic inputs; no compute)
 __all__ = ["inputs", "q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8", "mmq_q6K_q8",
            "mmq_q4K_isums", "mmq_q6K_isums", "q6K_prep_bytes", "q6K_prepare", "mmq_q6K_prep_q8",
            "mmq_q6K_prep_isums", "q6K_exp_bytes", "q6K_expand", "mmq_q6K_exp_q8", "mmq_q6K_exp_csums",
-           "QPGError"]
+           "mmq_sk_bytes", "mmq_q4K_q8_sk", "mmq_q6K_q8_sk", "mmq_q6K_prep_q8_sk", "mmq_q6K_exp_q8_sk", "QPGError"]
 
 
 def __getattr__(name):

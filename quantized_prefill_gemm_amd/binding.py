@@ -53,6 +53,11 @@ def lib() -> ctypes.CDLL:
         L.q6K_expand.argtypes = [P, P, I64, I64, P]
         for f in (L.mmq_q6K_exp_q8, L.mmq_q6K_exp_csums):
             f.argtypes = [P, P, P, I64, I64, I64, P]
+        L.qpg_mmq_sk_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
+        L.qpg_mmq_sk_bytes.restype = ctypes.c_size_t
+        for f in (L.mmq_q4K_q8_sk, L.mmq_q6K_q8_sk, L.mmq_q6K_prep_q8_sk, L.mmq_q6K_exp_q8_sk):
+            f.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+            f.restype = ctypes.c_int
         for f in (L.quantize_q8_1, L.mmq_q4K, L.mmq_q6K, L.mmq_q4K_q8, L.mmq_q6K_q8, L.mmq_q4K_isums,
                   L.mmq_q6K_isums, L.q6K_prepare, L.mmq_q6K_prep_q8, L.mmq_q6K_prep_isums, L.q6K_expand,
                   L.mmq_q6K_exp_q8, L.mmq_q6K_exp_csums):
@@ -64,7 +69,8 @@ def lib() -> ctypes.CDLL:
 EXPORTS = ("qpg_strerror", "qpg_q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6K", "mmq_q4K_q8",
            "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums", "qpg_q6K_prep_bytes", "q6K_prepare",
            "mmq_q6K_prep_q8", "mmq_q6K_prep_isums", "qpg_q6K_exp_bytes", "q6K_expand", "mmq_q6K_exp_q8",
-           "mmq_q6K_exp_csums")
+           "mmq_q6K_exp_csums", "qpg_mmq_sk_bytes", "mmq_q4K_q8_sk", "mmq_q6K_q8_sk", "mmq_q6K_prep_q8_sk",
+           "mmq_q6K_exp_q8_sk")
 
 
 def _check(rc: int, what: str):
@@ -273,3 +279,55 @@ def mmq_q6K_exp_q8(we, xq, M, N, K, y=None, stream=None):
 
 def mmq_q6K_exp_csums(we, xq, M, N, K, s=None, stream=None):
     return _mmq_exp(we, xq, M, N, K, s, stream, True)
+
+
+# Weight forms of the K-split entry points (the form argument of qpg_mmq_sk_bytes).
+SK_FORMS = {"q4K": 0, "q6K": 1, "q6K_prep": 2, "q6K_exp": 3}
+_SK_FN = {"q4K": "mmq_q4K_q8_sk", "q6K": "mmq_q6K_q8_sk", "q6K_prep": "mmq_q6K_prep_q8_sk",
+          "q6K_exp": "mmq_q6K_exp_q8_sk"}
+
+
+def mmq_sk_bytes(M: int, N: int, K: int, form: str) -> int:
+    """Workspace bytes of the K-split entry point for this shape (0: no split is made)."""
+    return int(lib().qpg_mmq_sk_bytes(M, N, K, SK_FORMS[form]))
+
+
+def _mmq_sk(form: str, w, xq, M, N, K, y, ws, stream):
+    _dev(xq, torch.uint8, "xq")
+    if xq.numel() < q8_1_bytes(M, K):
+        raise QPGError(QPG_EINVAL, "xq too small")
+    if form in ("q4K", "q6K"):
+        _wcheck(w, N, K, 144 if form == "q4K" else 210)
+    else:
+        _dev(w, torch.uint8, "w")
+        need = q6K_prep_bytes(N, K) if form == "q6K_prep" else q6K_exp_bytes(N, K)
+        if w.numel() < need:
+            raise QPGError(QPG_EINVAL, "w too small")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _dev(y, torch.float32, "y")
+    nws = mmq_sk_bytes(M, N, K, form)
+    if ws is None and nws:
+        ws = torch.empty(nws // 4, dtype=torch.float32, device=xq.device)
+    if ws is not None:
+        _dev(ws, torch.float32, "ws")
+    wsb = 0 if ws is None else ws.numel() * 4
+    _check(getattr(lib(), _SK_FN[form])(_ptr(w), _ptr(xq), _ptr(y), M, N, K, _ptr(ws), wsb, _stream(stream)),
+           _SK_FN[form])
+    return y
+
+
+def mmq_q4K_q8_sk(w, xq, M, N, K, y=None, ws=None, stream=None):
+    return _mmq_sk("q4K", w, xq, M, N, K, y, ws, stream)
+
+
+def mmq_q6K_q8_sk(w, xq, M, N, K, y=None, ws=None, stream=None):
+    return _mmq_sk("q6K", w, xq, M, N, K, y, ws, stream)
+
+
+def mmq_q6K_prep_q8_sk(wp, xq, M, N, K, y=None, ws=None, stream=None):
+    return _mmq_sk("q6K_prep", wp, xq, M, N, K, y, ws, stream)
+
+
+def mmq_q6K_exp_q8_sk(we, xq, M, N, K, y=None, ws=None, stream=None):
+    return _mmq_sk("q6K_exp", we, xq, M, N, K, y, ws, stream)

@@ -73,8 +73,8 @@ int mmq_checked(bool q6, const void* w, const void* xq, float* y, int32_t* s, in
         return QPG_EALIGN;
     rc = check_device();
     if (rc != QPG_OK) return rc;
-    return status_of(q6 ? qpg_launch_mmq_q6K(w, xq, y, s, M, N, K, st)
-                        : qpg_launch_mmq_q4K(w, xq, y, s, M, N, K, st));
+    return status_of(q6 ? qpg_launch_mmq_q6K(w, xq, y, s, M, N, K, 1, st)
+                        : qpg_launch_mmq_q4K(w, xq, y, s, M, N, K, 1, st));
 }
 
 // Prepared q6_K: the per-tile record offsets (nsb * 32 KiB) must stay below 2^31.
@@ -97,7 +97,7 @@ int mmq_prep_checked(const void* wp, const void* xq, float* y, int32_t* s, int64
     if (!aligned(wp, 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4))) return QPG_EALIGN;
     rc = check_device();
     if (rc != QPG_OK) return rc;
-    return status_of(qpg_launch_mmq_q6K_prep(wp, xq, y, s, M, N, K, st));
+    return status_of(qpg_launch_mmq_q6K_prep(wp, xq, y, s, M, N, K, 1, st));
 }
 
 // Expanded q6_K: the per-tile record range (nsb * 35,072 bytes) must stay below 2^31.
@@ -121,12 +121,100 @@ int mmq_exp_checked(const void* we, const void* xq, float* y, int32_t* s, int64_
     if (!aligned(we, 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4))) return QPG_EALIGN;
     rc = check_device();
     if (rc != QPG_OK) return rc;
-    return status_of(qpg_launch_mmq_q6K_exp(we, xq, y, s, M, N, K, st));
+    return status_of(qpg_launch_mmq_q6K_exp(we, xq, y, s, M, N, K, 1, st));
+}
+
+// ---- K split over workgroups for shapes with few tiles (at most 128: fewer than half the
+// CUs busy). Each piece is a contiguous super-block range of >= 3 super-blocks (so each of a
+// workgroup's three groups still gets one), and the pieces together fill at most one
+// workgroup per CU.
+constexpr int kSkMaxPieces = 8;
+
+int64_t form_tiles(int form, int64_t M, int64_t N)
+{
+    const int64_t tn = form == 3 ? 64 : 128;                  // expanded q6_K uses 64-row tiles
+    return ((M + 63) / 64) * ((N + tn - 1) / tn);
+}
+
+int sk_pieces(int form, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t tiles = form_tiles(form, M, N);
+    if (tiles > 128) return 1;
+    int64_t p = 256 / tiles;
+    p = p < kSkMaxPieces ? p : kSkMaxPieces;
+    const int64_t by_k = (K / 256) / 3;
+    p = p < by_k ? p : by_k;
+    return p > 1 ? (int)p : 1;
+}
+
+bool form_shape_ok(int form, int64_t M, int64_t N, int64_t K)
+{
+    if (check_mmq_shape(M, N, K) != QPG_OK) return false;
+    if (form == 2) return prep_shape_ok(N, K);
+    if (form == 3) return exp_shape_ok(N, K) && form_tiles(3, M, N) < kMaxDim;
+    return form >= 0 && form <= 1;
+}
+
+int mmq_sk_checked(int form, const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                   size_t ws_bytes, hipStream_t st)
+{
+    if (!w || !xq || !y) return QPG_EINVAL;
+    if (!form_shape_ok(form, M, N, K)) return QPG_EINVAL;
+    const int P = sk_pieces(form, M, N, K);
+    if (P > 1) {
+        if (!ws || ws_bytes < (size_t)P * (size_t)M * (size_t)N * 4) return QPG_EINVAL;
+        if (!aligned(ws, 16)) return QPG_EALIGN;
+    }
+    const uintptr_t wa = form == 1 ? 4 : 16;
+    if (!aligned(w, wa) || !aligned(xq, 16) || !aligned(y, 4)) return QPG_EALIGN;
+    const int rc = check_device();
+    if (rc != QPG_OK) return rc;
+    float* out = P > 1 ? static_cast<float*>(ws) : y;
+    hipError_t e;
+    switch (form) {
+    case 0: e = qpg_launch_mmq_q4K(w, xq, out, nullptr, M, N, K, P, st); break;
+    case 1: e = qpg_launch_mmq_q6K(w, xq, out, nullptr, M, N, K, P, st); break;
+    case 2: e = qpg_launch_mmq_q6K_prep(w, xq, out, nullptr, M, N, K, P, st); break;
+    default: e = qpg_launch_mmq_q6K_exp(w, xq, out, nullptr, M, N, K, P, st); break;
+    }
+    if (e == hipSuccess && P > 1) e = qpg_launch_splitk_reduce(static_cast<const float*>(ws), y, M * N, P, st);
+    return status_of(e);
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t qpg_mmq_sk_bytes(int64_t M, int64_t N, int64_t K, int form)
+{
+    if (form < 0 || form > 3 || !form_shape_ok(form, M, N, K)) return 0;
+    const int P = sk_pieces(form, M, N, K);
+    return P > 1 ? (size_t)P * (size_t)M * (size_t)N * 4 : 0;
+}
+
+int mmq_q4K_q8_sk(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                  size_t ws_bytes, qpg_stream_t stream)
+{
+    return mmq_sk_checked(0, w, xq, y, M, N, K, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_q8_sk(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                  size_t ws_bytes, qpg_stream_t stream)
+{
+    return mmq_sk_checked(1, w, xq, y, M, N, K, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_prep_q8_sk(const void* wp, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                       size_t ws_bytes, qpg_stream_t stream)
+{
+    return mmq_sk_checked(2, wp, xq, y, M, N, K, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+int mmq_q6K_exp_q8_sk(const void* we, const void* xq, float* y, int64_t M, int64_t N, int64_t K, void* ws,
+                      size_t ws_bytes, qpg_stream_t stream)
+{
+    return mmq_sk_checked(3, we, xq, y, M, N, K, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
 
 size_t qpg_q6K_exp_bytes(int64_t N, int64_t K)
 {

@@ -81,17 +81,20 @@ static_assert(4 * (AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= TM * TN * 4, "a group's stag
 // Source offset of a pad slot: past every buffer's range, so the load writes zeros.
 constexpr unsigned PAD_OFF = 0x7F000000u;
 
-__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
+__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int& piece, int tiles_m, int total,
+                                            int pieces)
 {
     // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Give each XCD a
-    // contiguous range of tiles, M fastest, so the workgroups sharing a weight tile run
-    // on one XCD and read it into that XCD's L2 once.
-    const int bid = blockIdx.x;
+    // contiguous range of (tile, K-piece) units, M fastest, so the workgroups sharing a
+    // weight tile run on one XCD and read it into that XCD's L2 once.
+    const int bid = blockIdx.x, units = total * pieces;
     const int xcd = bid & 7, k = bid >> 3;
-    const int q = total >> 3, r = total & 7;
+    const int q = units >> 3, r = units & 7;
     const int t = xcd * q + (xcd < r ? xcd : r) + k;
-    m_tile = t % tiles_m;
-    n_tile = t / tiles_m;
+    const int tile = t % total;
+    piece = t / total;
+    m_tile = tile % tiles_m;
+    n_tile = tile / tiles_m;
 }
 
 // Position of weight row jj (0..31 inside a wave's rows) in C-register order: k-group
@@ -121,11 +124,14 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
                                                          const uint32_t* __restrict__ hdr,
                                                          float* __restrict__ Y,
                                                          int32_t* __restrict__ S,
-                                                         int M, int N, int K, int tiles_m, int total)
+                                                         int M, int N, int K, int tiles_m, int total, int pieces)
 {
     __shared__ GroupLds lds_all[KS];
-    int m_tile, n_tile;
-    tile_coords(m_tile, n_tile, tiles_m, total);
+    int m_tile, n_tile, piece;
+    tile_coords(m_tile, n_tile, piece, tiles_m, total, pieces);
+    // K-split over workgroups (few tiles): piece p adds the super-blocks [p*nsb/P, (p+1)*nsb/P)
+    // and writes its partial tile to Y + p*M*N (a workspace the caller sums in piece order).
+    if (pieces > 1) Y += (size_t)piece * M * N;
     const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
     GroupLds& L = lds_all[grp];
     const int tid = threadIdx.x & 255, lane = tid & 63;        // thread index inside the group
@@ -363,8 +369,9 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
     // This group's super-blocks: [sb0, sb0 + cnt). Every group runs the same number of
     // iterations (all waves of the workgroup meet at each barrier); a group with one
     // super-block fewer idles through its last one.
-    const int nbase = nsb / KS, nrem = nsb % KS;
-    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
+    const int pb0 = (int)(((int64_t)piece * nsb) / pieces), pcnt = (int)(((int64_t)(piece + 1) * nsb) / pieces) - pb0;
+    const int nbase = pcnt / KS, nrem = pcnt % KS;
+    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = pb0 + grp * nbase + min(grp, nrem);
     const int iters = nbase + (nrem ? 1 : 0);
     uint32x4 hv;
     if (cnt > 0) {
@@ -454,7 +461,7 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
 }  // namespace qpg
 
 hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
-                              int64_t K, hipStream_t s)
+                              int64_t K, int pieces, hipStream_t s)
 {
     using namespace qpg::q4k;
     const int tiles_m = (int)((M + TM - 1) / TM);
@@ -465,21 +472,22 @@ hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* 
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     // At most one tile per CU (256 CUs): split each tile's super-blocks over three
     // four-wave groups, so each SIMD still holds three waves.
-    const bool split = total <= 256 && K / 256 >= 3;
+    const bool split = total * pieces <= 256 && (K / 256) / pieces >= 3;
+    const unsigned grid = (unsigned)(total * pieces);
     if (isums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q4K_kernel<true, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 3>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q4K_kernel<true, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 1>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q4K_kernel<false, 3>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 3>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q4K_kernel<false, 1>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y, isums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 1>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
     }
     return hipGetLastError();
 }

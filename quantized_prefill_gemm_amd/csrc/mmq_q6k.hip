@@ -68,16 +68,20 @@ __device__ __forceinline__ int aq_sw(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int bl_sw(int j) { return (j >> 2) & 3; }
 __device__ __forceinline__ int bh_sw(int j) { return (j >> 3) & 1; }
 
-__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
+__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int& piece, int tiles_m, int total,
+                                            int pieces)
 {
-    // round-robin XCD dispatch: give each XCD a contiguous range of tiles, M fastest, so
-    // the workgroups sharing a weight tile run on one XCD (one L2)
-    const int bid = blockIdx.x;
+    // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Give each XCD a
+    // contiguous range of (tile, K-piece) units, M fastest, so the workgroups sharing a
+    // weight tile run on one XCD and read it into that XCD's L2 once.
+    const int bid = blockIdx.x, units = total * pieces;
     const int xcd = bid & 7, k = bid >> 3;
-    const int q = total >> 3, r = total & 7;
+    const int q = units >> 3, r = units & 7;
     const int t = xcd * q + (xcd < r ? xcd : r) + k;
-    m_tile = t % tiles_m;
-    n_tile = t / tiles_m;
+    const int tile = t % total;
+    piece = t / total;
+    m_tile = tile % tiles_m;
+    n_tile = tile / tiles_m;
 }
 
 __device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
@@ -116,11 +120,14 @@ static_assert(offsetof(StageLds, bh) == offsetof(StageLds, bl) + TN * 64 &&
 template <bool ISUMS, int KS, bool PREP>
 __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
-    float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total)
+    float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total, int pieces)
 {
     __shared__ GroupLds lds_all[KS];
-    int m_tile, n_tile;
-    tile_coords(m_tile, n_tile, tiles_m, total);
+    int m_tile, n_tile, piece;
+    tile_coords(m_tile, n_tile, piece, tiles_m, total, pieces);
+    // K-split over workgroups (few tiles): piece p adds the super-blocks [p*nsb/P, (p+1)*nsb/P)
+    // and writes its partial tile to Y + p*M*N (a workspace the caller sums in piece order).
+    if (pieces > 1) Y += (size_t)piece * M * N;
     const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
     GroupLds& G = lds_all[grp];
     const int tid = threadIdx.x & 255, lane = tid & 63;        // thread index inside the group
@@ -313,8 +320,9 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_k
 
     // Pipeline over this group's stages: super-blocks [sb0, sb0 + cnt), two stages each.
     // Every group runs the same number of stages so that all waves meet at every barrier.
-    const int nbase = nsb / KS, nrem = nsb % KS;
-    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
+    const int pb0 = (int)(((int64_t)piece * nsb) / pieces), pcnt = (int)(((int64_t)(piece + 1) * nsb) / pieces) - pb0;
+    const int nbase = pcnt / KS, nrem = pcnt % KS;
+    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = pb0 + grp * nbase + min(grp, nrem);
     const int nst = 2 * cnt, nst_all = 2 * (nbase + (nrem ? 1 : 0));
     Pre pre;
     (void)pre;
@@ -449,7 +457,7 @@ __global__ void __launch_bounds__(256) q6K_prepare_kernel(const uint8_t* __restr
 namespace {
 template <bool PREP>
 hipError_t launch_q6K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N, int64_t K,
-                      hipStream_t s)
+                      int pieces, hipStream_t s)
 {
     using namespace qpg::q6k;
     const int tiles_m = (int)((M + TM - 1) / TM);
@@ -459,36 +467,37 @@ hipError_t launch_q6K(const void* w, const void* xq, float* y, int32_t* isums, i
     const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     // At most one tile per CU (256 CUs): split each tile's super-blocks over three groups.
-    const bool split = total <= 256 && K / 256 >= 3;
+    const bool split = total * pieces <= 256 && (K / 256) / pieces >= 3;
+    const unsigned grid = (unsigned)(total * pieces);
     if (isums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_kernel<true, 3, PREP>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y,
-                               isums, (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 3, PREP>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q6K_kernel<true, 1, PREP>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y,
-                               isums, (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<true, 1, PREP>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total, pieces);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_kernel<false, 3, PREP>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y,
-                               isums, (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 3, PREP>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q6K_kernel<false, 1, PREP>), dim3(total), dim3(256), 0, s, wb, qplane, hdr, y,
-                               isums, (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_kernel<false, 1, PREP>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y,
+                               isums, (int)M, (int)N, (int)K, tiles_m, total, pieces);
     }
     return hipGetLastError();
 }
 }  // namespace
 
 hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
-                              int64_t K, hipStream_t s)
+                              int64_t K, int pieces, hipStream_t s)
 {
-    return launch_q6K<false>(w, xq, y, isums, M, N, K, s);
+    return launch_q6K<false>(w, xq, y, isums, M, N, K, pieces, s);
 }
 
 hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
-                                   int64_t K, hipStream_t s)
+                                   int64_t K, int pieces, hipStream_t s)
 {
-    return launch_q6K<true>(wp, xq, y, isums, M, N, K, s);
+    return launch_q6K<true>(wp, xq, y, isums, M, N, K, pieces, s);
 }
 
 hipError_t qpg_launch_q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, hipStream_t s)

@@ -79,16 +79,20 @@ __device__ __forceinline__ int aq_sw(int t) { return (t >> 1) & 7; }
 // registers r = 0..15 of rows 8(r>>2) + 4hg + (r&3) at 16 hg + r.
 __device__ __forceinline__ int c_pos(int jj) { return 16 * ((jj >> 2) & 1) + 4 * (jj >> 3) + (jj & 3); }
 
-__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int tiles_m, int total)
+__device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int& piece, int tiles_m, int total,
+                                            int pieces)
 {
-    // round-robin XCD dispatch: each XCD gets a contiguous range of tiles, M fastest, so the
-    // workgroups sharing a weight tile run on one XCD (one L2)
-    const int bid = blockIdx.x;
+    // Workgroups are dispatched round-robin over the 8 XCDs (bid % 8). Give each XCD a
+    // contiguous range of (tile, K-piece) units, M fastest, so the workgroups sharing a
+    // weight tile run on one XCD and read it into that XCD's L2 once.
+    const int bid = blockIdx.x, units = total * pieces;
     const int xcd = bid & 7, k = bid >> 3;
-    const int q = total >> 3, r = total & 7;
+    const int q = units >> 3, r = units & 7;
     const int t = xcd * q + (xcd < r ? xcd : r) + k;
-    m_tile = t % tiles_m;
-    n_tile = t / tiles_m;
+    const int tile = t % total;
+    piece = t / total;
+    m_tile = tile % tiles_m;
+    n_tile = tile / tiles_m;
 }
 
 // Wait for this wave's outstanding vector-memory operations (the LDS-direct loads).
@@ -114,13 +118,16 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_w
 template <bool CSUMS, int KS, int KW>
 __global__ void __launch_bounds__(256 * KS * KW, (CSUMS || KS > 1) ? 1 : (KW > 1 ? 2 : 3)) mmq_q6K_exp_kernel(
     const uint8_t* __restrict__ WE, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
-    float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total)
+    float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total, int pieces)
 {
     static_assert(KS == 1 || KW == 1, "a K split over groups or over waves, not both");
     constexpr int NW = 4 * KW;                      // waves sharing one set of stage buffers
     __shared__ GroupLds lds_all[KS];
-    int m_tile, n_tile;
-    tile_coords(m_tile, n_tile, tiles_m, total);
+    int m_tile, n_tile, piece;
+    tile_coords(m_tile, n_tile, piece, tiles_m, total, pieces);
+    // K-split over workgroups (few tiles): piece p adds the super-blocks [p*nsb/P, (p+1)*nsb/P)
+    // and writes its partial tile to Y + p*M*N (a workspace the caller sums in piece order).
+    if (pieces > 1) Y += (size_t)piece * M * N;
     const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
     GroupLds& G = lds_all[grp];
     const int tid = threadIdx.x & (64 * NW - 1), lane = tid & 63;
@@ -274,8 +281,9 @@ __global__ void __launch_bounds__(256 * KS * KW, (CSUMS || KS > 1) ? 1 : (KW > 1
 
     // Pipeline over this group's stages: super-blocks [sb0, sb0 + cnt), two stages each.
     // Every group runs the same number of stages so that all waves meet at every barrier.
-    const int nbase = nsb / KS, nrem = nsb % KS;
-    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = grp * nbase + min(grp, nrem);
+    const int pb0 = (int)(((int64_t)piece * nsb) / pieces), pcnt = (int)(((int64_t)(piece + 1) * nsb) / pieces) - pb0;
+    const int nbase = pcnt / KS, nrem = pcnt % KS;
+    const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = pb0 + grp * nbase + min(grp, nrem);
     const int iters = nbase + (nrem ? 1 : 0);
     // Stage (sb, 0) lives in buffer 0 and (sb, 1) in buffer 1, so every LDS address of the
     // compute is a lane offset plus an immediate.
@@ -418,7 +426,7 @@ hipError_t qpg_launch_q6K_expand(const void* w, void* we, int64_t N, int64_t K, 
 }
 
 hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int32_t* csums, int64_t M, int64_t N,
-                                  int64_t K, hipStream_t s)
+                                  int64_t K, int pieces, hipStream_t s)
 {
     using namespace qpg::q6kx;
     const int tiles_m = (int)((M + TM - 1) / TM);
@@ -429,21 +437,22 @@ hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int3
     const uint8_t* wb = static_cast<const uint8_t*>(we);
     // At most one tile per CU: split each tile's super-blocks over three groups; otherwise
     // eight waves per tile (two per SIMD) split each stage's chunks.
-    const bool split = total <= 256 && K / 256 >= 3;
+    const bool split = total * pieces <= 256 && (K / 256) / pieces >= 3;
+    const unsigned grid = (unsigned)(total * pieces);
     if (csums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 3, 1>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 3, 1>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, csums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 1, 2>), dim3(total), dim3(512), 0, s, wb, qplane, hdr, y, csums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<true, 1, 2>), dim3(grid), dim3(512), 0, s, wb, qplane, hdr, y, csums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 3, 1>), dim3(total), dim3(768), 0, s, wb, qplane, hdr, y, csums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 3, 1>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, csums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 1, 2>), dim3(total), dim3(512), 0, s, wb, qplane, hdr, y, csums,
-                               (int)M, (int)N, (int)K, tiles_m, total);
+            hipLaunchKernelGGL((mmq_q6K_exp_kernel<false, 1, 2>), dim3(grid), dim3(512), 0, s, wb, qplane, hdr, y, csums,
+                               (int)M, (int)N, (int)K, tiles_m, total, pieces);
     }
     return hipGetLastError();
 }

@@ -51,15 +51,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 // Kernel launchers (defined in the .hip files; called by the C ABI layer after the
 // arguments have been validated). They return hipGetLastError() of the launch.
 hipError_t qpg_launch_quantize_q8_1(const float* x, void* xq, int64_t M, int64_t K, hipStream_t s);
+// pieces > 1: K split over workgroups, y is then a [pieces][M][N] f32 workspace of partial
+// sums (qpg_launch_splitk_reduce adds them); pieces = 1: y is the output.
 hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* isums,
-                              int64_t M, int64_t N, int64_t K, hipStream_t s);
+                              int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K(const void* w, const void* xq, float* y, int32_t* isums,
-                              int64_t M, int64_t N, int64_t K, hipStream_t s);
+                              int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s);
 // q6_K prepared layout: ceil(N/128) * (K/256) * 32 KiB (layout in mmq_q6k.hip)
 hipError_t qpg_launch_q6K_prepare(const void* w, void* wp, int64_t N, int64_t K, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int32_t* isums,
-                                   int64_t M, int64_t N, int64_t K, hipStream_t s);
-// q6_K expanded layout: ceil(N/64) * (K/256) * 33,024 bytes (layout in mmq_q6k_exp.hip)
+                                   int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s);
+// q6_K expanded layout: ceil(N/64) * (K/256) * 35,072 bytes (layout in mmq_q6k_exp.hip)
 hipError_t qpg_launch_q6K_expand(const void* w, void* we, int64_t N, int64_t K, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int32_t* csums,
-                                  int64_t M, int64_t N, int64_t K, hipStream_t s);
+                                  int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s);
+// y[i] = sum over p < pieces of ws[p * MN + i], in piece order (deterministic).
+hipError_t qpg_launch_splitk_reduce(const float* ws, float* y, int64_t MN, int pieces, hipStream_t s);

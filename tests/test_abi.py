@@ -46,6 +46,10 @@ def L():
     lib.q6K_expand.argtypes = [P, P, I64, I64, P]
     for f in (lib.mmq_q6K_exp_q8, lib.mmq_q6K_exp_csums):
         f.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.qpg_mmq_sk_bytes.restype = ctypes.c_size_t
+    lib.qpg_mmq_sk_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
+    for f in (lib.mmq_q4K_q8_sk, lib.mmq_q6K_q8_sk, lib.mmq_q6K_prep_q8_sk, lib.mmq_q6K_exp_q8_sk):
+        f.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     return lib
 
 
@@ -154,6 +158,36 @@ def test_q6K_expand_sizes_and_rejects(L):
     assert L.mmq_q6K_exp_csums(A16, A16, A2, 64, 256, 256, None) == EALIGN
 
 
+def test_splitk_workspace_sizes(L):
+    # P = min(8, 256 // tiles, (K/256) // 3) when tiles <= 128, else no split (0 bytes)
+    assert L.qpg_mmq_sk_bytes(512, 512, 4096, 0) == 5 * 512 * 512 * 4      # 32 tiles, 16 SB -> 5
+    assert L.qpg_mmq_sk_bytes(512, 1376, 4096, 0) == 2 * 512 * 1376 * 4    # 88 tiles -> 2
+    assert L.qpg_mmq_sk_bytes(512, 512, 11008, 1) == 8 * 512 * 512 * 4     # 32 tiles, 43 SB -> 8
+    assert L.qpg_mmq_sk_bytes(512, 512, 11008, 2) == 8 * 512 * 512 * 4
+    assert L.qpg_mmq_sk_bytes(512, 512, 11008, 3) == 4 * 512 * 512 * 4     # 64 tiles of 64 x 64 -> 4
+    assert L.qpg_mmq_sk_bytes(64, 100, 1536, 0) == 2 * 64 * 100 * 4        # 1 tile, 6 SB -> 2
+    assert L.qpg_mmq_sk_bytes(512, 11008, 4096, 0) == 0                    # 688 tiles
+    assert L.qpg_mmq_sk_bytes(512, 1024, 4096, 3) == 2 * 512 * 1024 * 4    # 128 tiles -> 256 / 128 = 2
+    assert L.qpg_mmq_sk_bytes(512, 1088, 4096, 3) == 0                     # 136 tiles of 64 x 64
+    assert L.qpg_mmq_sk_bytes(64, 128, 1280, 0) == 0                       # 5 SB: < 3 per piece
+    for form in (-1, 4):
+        assert L.qpg_mmq_sk_bytes(512, 512, 4096, form) == 0
+    assert L.qpg_mmq_sk_bytes(512, 512, 300, 0) == 0
+    assert L.qpg_mmq_sk_bytes(0, 512, 4096, 0) == 0
+
+
+def test_splitk_rejects(L):
+    need = L.qpg_mmq_sk_bytes(512, 512, 4096, 0)
+    assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, None, need, None) == EINVAL      # no workspace
+    assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A16, need - 4, None) == EINVAL  # too small
+    assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A8, need, None) == EALIGN
+    assert L.mmq_q4K_q8_sk(A8, A16, A16, 512, 512, 4096, A16, need, None) == EALIGN
+    assert L.mmq_q6K_q8_sk(A2, A16, A16, 512, 512, 4096, A16, need, None) == EALIGN       # q6_K: 4 bytes
+    assert L.mmq_q6K_prep_q8_sk(A16, A16, A16, 512, 512, 1 << 24, A16, need, None) == EINVAL
+    assert L.mmq_q6K_exp_q8_sk(None, A16, A16, 512, 512, 4096, A16, need, None) == EINVAL
+    assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 512, 512, 288, A16, need, None) == EINVAL
+
+
 def _has_gpu():
     try:
         import torch
@@ -172,6 +206,9 @@ def test_valid_call_without_device_reports_edevice(L):
     assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
     assert L.q6K_expand(A2, A16, 64, 256, None) == EDEVICE          # raw blocks: any alignment
     assert L.mmq_q6K_exp_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
+    # no split for this shape: the workspace may be absent
+    assert L.mmq_q4K_q8_sk(A16, A16, A16, 64, 256, 1280, None, 0, None) == EDEVICE
+    assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 64, 256, 4096, A16, 5 * 64 * 256 * 4, None) == EDEVICE
 
 
 CALIB = os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so")

@@ -279,6 +279,101 @@ def test_q6K_exp_config4_full():
     assert np.array_equal(s.cpu().numpy(), O.q6K_chunk_sums(Wr, q))
 
 
+# ----------------------------------------------------------------------------- K split over workgroups
+
+SK_FORMS = ["q4K", "q6K", "q6K_prep", "q6K_exp"]
+SK_SHAPES = [(1, 1, 1536), (64, 100, 1536), (33, 130, 2816), (100, 300, 4096), (130, 257, 11008)]
+BPB = {"q4_K": 144, "q6_K": 210}
+
+
+def sk_operands(form, W, N, K):
+    if form == "q6K_prep":
+        return gpu_prepare(W, N, K)
+    if form == "q6K_exp":
+        return gpu_expand(W, N, K)
+    return dev(W.reshape(-1))
+
+
+def sk_call(form, w, xq, M, N, K, y=None, ws=None):
+    fn = {"q4K": B.mmq_q4K_q8_sk, "q6K": B.mmq_q6K_q8_sk, "q6K_prep": B.mmq_q6K_prep_q8_sk,
+          "q6K_exp": B.mmq_q6K_exp_q8_sk}[form]
+    return fn(w, xq, M, N, K, y=y, ws=ws)
+
+
+def plain_call(form, w, xq, M, N, K):
+    fn = {"q4K": B.mmq_q4K_q8, "q6K": B.mmq_q6K_q8, "q6K_prep": B.mmq_q6K_prep_q8,
+          "q6K_exp": B.mmq_q6K_exp_q8}[form]
+    return fn(w, xq, M, N, K)
+
+
+@pytest.mark.parametrize("form", SK_FORMS)
+@pytest.mark.parametrize("M,N,K", SK_SHAPES)
+def test_splitk_matches_oracle(form, M, N, K):
+    """K split over P workgroups: y against the oracle; plane p of the workspace against the
+    oracle on super-blocks [p*nsb/P, (p+1)*nsb/P) alone; y is the piece-order f32 sum of the
+    planes, bit for bit, and the same on a second call."""
+    wtype = "q4_K" if form == "q4K" else "q6_K"
+    nws = B.mmq_sk_bytes(M, N, K, form)
+    P = nws // (4 * M * N)
+    say(f"[split-K {form} {M}x{N}x{K} pieces {P}]")
+    assert P >= 2 and nws == P * M * N * 4
+    W, X = inputs.small_case(wtype, M, N, K, seed=9, gain=True)
+    xq, _ = gpu_quantize(X)
+    w = sk_operands(form, W, N, K)
+    ws = torch.full((nws // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    y1 = sk_call(form, w, xq, M, N, K, ws=ws)
+    torch.cuda.synchronize()
+    planes = ws.view(P, M, N).cpu().numpy()
+    y2 = sk_call(form, w, xq, M, N, K, ws=ws)
+    torch.cuda.synchronize()
+    g = y1.cpu().numpy()
+    assert np.array_equal(g, y2.cpu().numpy())
+    check_out(g, O.mmq(wtype, W, X), f"sk {form} {M}x{N}x{K}")
+    acc = planes[0].copy()
+    for p in range(1, P):
+        acc = acc + planes[p]
+    assert np.array_equal(acc, g)
+    nsb = K // 256
+    Wb = W.reshape(N, nsb, BPB[wtype])
+    for p in range(P):
+        b0, b1 = p * nsb // P, (p + 1) * nsb // P
+        Wp = np.ascontiguousarray(Wb[:, b0:b1]).reshape(N, -1)
+        rp = O.mmq(wtype, Wp, np.ascontiguousarray(X[:, 256 * b0:256 * b1]))
+        check_out(planes[p], rp, f"  piece {p} (super-blocks {b0}..{b1 - 1})")
+
+
+@pytest.mark.parametrize("form", SK_FORMS)
+def test_splitk_without_split_is_the_plain_entry(form):
+    """Shapes that need no split (many tiles, or < 6 super-blocks) take no workspace and
+    give the plain entry point's output bit for bit."""
+    wtype = "q4_K" if form == "q4K" else "q6_K"
+    for M, N, K in ((64, 100, 1280), (640, 2100, 1024)):
+        assert B.mmq_sk_bytes(M, N, K, form) == 0
+        say(f"[split-K no split {form} {M}x{N}x{K}]")
+        W, X = inputs.small_case(wtype, M, N, K, seed=10)
+        xq, _ = gpu_quantize(X)
+        w = sk_operands(form, W, N, K)
+        y = sk_call(form, w, xq, M, N, K)
+        y0 = plain_call(form, w, xq, M, N, K)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), y0.cpu().numpy())
+
+
+@pytest.mark.parametrize("form,N,K", [("q4K", 1376, 4096), ("q4K", 512, 4096), ("q6K", 512, 11008),
+                                      ("q6K_prep", 512, 11008), ("q6K_exp", 512, 11008)])
+def test_splitk_shard_shapes(form, N, K):
+    """One GPU's share of a 7B-style layer split eight ways along N (M = 512 prompt tokens),
+    the shapes the split is for: full output against the oracle."""
+    wtype = "q4_K" if form == "q4K" else "q6_K"
+    M = 512
+    say(f"[split-K shard {form} {M}x{N}x{K} pieces {B.mmq_sk_bytes(M, N, K, form) // (4 * M * N)}]")
+    W, X = inputs.small_case(wtype, M, N, K, seed=11, gain=True)
+    xq, _ = gpu_quantize(X)
+    y = sk_call(form, sk_operands(form, W, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq(wtype, W, X), f"shard {form}")
+
+
 def test_closed_form_scale_path_on_gpu():
     """All nib = 1, sc = 1, d = 1, X = 1: Y = K * 0.99993896484375 exactly (golden)."""
     K = 1024
@@ -303,14 +398,18 @@ def test_stack_sampled_rows():
 
 
 def test_graph_replay_matches_eager():
-    """A small two-layer stack (quantize + q4_K / q6_K / prepared / expanded q6_K GEMMs) captured as one
+    """A small two-layer stack (quantize + q4_K / q6_K / prepared / expanded q6_K GEMMs, one with
+    the K split) captured as one
     graph: every replay, with eager work and synchronisations between replays, must give
     the eager outputs bit for bit."""
     M = 96
-    specs = [("q4_K", 384, 512), ("q6_K", 256, 768), ("q6p", 200, 1024), ("q4_K", 130, 768), ("q6x", 190, 768)]
+    specs = [("q4_K", 384, 512), ("q6_K", 256, 768), ("q6p", 200, 1024), ("q4_K", 130, 768), ("q6x", 190, 768),
+             ("q4s", 200, 3072)]
     mats, xs, xqs, ys = [], [], [], []
+    ws = torch.empty(B.mmq_sk_bytes(M, 200, 3072, "q4K") // 4, dtype=torch.float32, device=DEV)
+    assert ws.numel() > 0
     for i, (kind, N, K) in enumerate(specs):
-        wtype = "q4_K" if kind == "q4_K" else "q6_K"
+        wtype = "q4_K" if kind in ("q4_K", "q4s") else "q6_K"
         W, X = inputs.small_case(wtype, M, N, K, seed=40 + i)
         w = dev(W.reshape(-1))
         if kind == "q6p":
@@ -331,6 +430,8 @@ def test_graph_replay_matches_eager():
                 B.mmq_q6K_q8(w, xq, M, N, K, y)
             elif kind == "q6p":
                 B.mmq_q6K_prep_q8(w, xq, M, N, K, y)
+            elif kind == "q4s":
+                B.mmq_q4K_q8_sk(w, xq, M, N, K, y, ws)
             else:
                 B.mmq_q6K_exp_q8(w, xq, M, N, K, y)
 
