@@ -8,7 +8,10 @@ synthetic data resident in HBM before timing starts.
 Prints ONE JSON line (metric, value in TMAC/s = M*N*K / step time, roofline of the MMQ
 kernel, CPU-oracle baseline). Defaults: 200 warm-up and 1000 timed steps (~100 ms of GPU
 time): the first ~10-20 ms of a run are up to 10 % slower while the clock ramps up.
-Other modes (for rocprofv3 runs):
+Other modes:
+  --shards                   the N/8 shares of the 7B layer GEMMs, plain vs K-split entry
+                             points (one JSON line per shape)
+For rocprofv3 runs:
   --profile {q4K,q6K,q6Kp,q6Kx,quant}  a few launches of one kernel (q6_K raw / prepared /
                              expanded), no timing output
   --copy-calibration         a device-to-device copy of known size (HBM counter scale)
@@ -300,6 +303,57 @@ def profile_mode(which: str, launches: int):
     print(f"profiled {which}: {launches} launches of {wtype} {M}x{N}x{K}", flush=True)
 
 
+SHARD_SHAPES = [("q4K", 512, 1376, 4096, "gate/up share"), ("q4K", 512, 512, 4096, "q/k/v/o share"),
+                ("q6K", 512, 512, 11008, "down share, raw q6_K"), ("q6K_prep", 512, 512, 11008, "down share, prepared"),
+                ("q6K_exp", 512, 512, 11008, "down share, expanded"), ("q4K", 128, 4096, 4096, "short prompt")]
+
+
+def run_shards(steps: int, warmup: int):
+    """One GPU's N/8 share of each 7B layer GEMM (M = 512) and a short prompt: the plain entry
+    point against the K-split entry point (partial tiles + reduce), HIP events around `steps`
+    back-to-back calls of each. One JSON line per shape."""
+    import torch
+    from quantized_prefill_gemm_amd import binding as B
+    from quantized_prefill_gemm_amd import inputs
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    for form, M, N, K, what in SHARD_SHAPES:
+        wtype = "q4_K" if form == "q4K" else "q6_K"
+        W, X = inputs.small_case(wtype, M, N, K, seed=1)
+        w = torch.from_numpy(W.reshape(-1)).to(dev)
+        if form == "q6K_prep":
+            w = B.q6K_prepare(w, N, K)
+        elif form == "q6K_exp":
+            w = B.q6K_expand(w, N, K)
+        xq = B.quantize_q8_1(torch.from_numpy(X).to(dev))
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        nws = B.mmq_sk_bytes(M, N, K, form)
+        ws = torch.empty(max(nws // 4, 1), dtype=torch.float32, device=dev)
+        plain = {"q4K": B.mmq_q4K_q8, "q6K": B.mmq_q6K_q8, "q6K_prep": B.mmq_q6K_prep_q8,
+                 "q6K_exp": B.mmq_q6K_exp_q8}[form]
+        sk = {"q4K": B.mmq_q4K_q8_sk, "q6K": B.mmq_q6K_q8_sk, "q6K_prep": B.mmq_q6K_prep_q8_sk,
+              "q6K_exp": B.mmq_q6K_exp_q8_sk}[form]
+        t = {}
+        for name, fn in (("plain", lambda: plain(w, xq, M, N, K, y, stream=stream)),
+                         ("split", lambda: sk(w, xq, M, N, K, y, ws if nws else None, stream=stream))):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[name] = e0.elapsed_time(e1) / steps * 1e3
+        macs = M * N * K
+        print(json.dumps({"shard": what, "form": form, "M": M, "N": N, "K": K,
+                          "pieces": nws // (4 * M * N) if nws else 1,
+                          "plain_us": round(t["plain"], 2), "split_us": round(t["split"], 2),
+                          "plain_tmacs": round(macs / t["plain"] / 1e6, 1),
+                          "split_tmacs": round(macs / t["split"] / 1e6, 1)}), flush=True)
+
+
 def copy_calibration(nbytes: int, launches: int):
     import torch
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -328,6 +382,8 @@ def main():
     ap.add_argument("--profile", choices=["q4K", "q6K", "q6Kp", "q6Kx", "quant"])
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--shards", action="store_true",
+                    help="time the N/8 shares of the 7B layer GEMMs: plain vs K-split entry points")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
@@ -338,6 +394,10 @@ def main():
         return
     if a.profile:
         profile_mode(a.profile, a.launches)
+        return
+    if a.shards:
+        run_shards(a.steps if a.steps != ap.get_default("steps") else 300,
+                   a.warmup if a.warmup != ap.get_default("warmup") else 100)
         return
 
     if a.config == 5:
@@ -408,9 +468,9 @@ def main():
                                          / mmq_s / 1e9, 1),
         "wall_s": round(r["wall_s"], 4),
     }
-    # The fold (2 f32 FMAs per output and 32-chunk for q4_K, 4 for q6_K) runs on the VALU, which
+    # The fold (2 f32 FMAs per output and 32-chunk for q4_K, 4 for q6_K, 3 for expanded q6_K) runs on the VALU, which
     # the matrix core does not overlap on this device; its share against the f32 vector peak.
-    fold_fma = M * N * (K // 32) * (2 if r["wtype"] == "q4_K" else 4)
+    fold_fma = M * N * (K // 32) * (2 if r["wtype"] == "q4_K" else 3 if q6 == "expanded" else 4)
     fold_tflops = 2 * fold_fma / mmq_s / 1e12
     out["fold_valu"] = {"achieved": round(fold_tflops, 2), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(fold_tflops / PEAK_F32_VALU_TFLOPS, 4),
