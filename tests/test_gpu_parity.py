@@ -374,6 +374,101 @@ def test_splitk_shard_shapes(form, N, K):
     check_out(y.cpu().numpy(), O.mmq(wtype, W, X), f"shard {form}")
 
 
+# ----------------------------------------------------------------------------- maximum sizes
+
+KMAX_RAW = 1 << 24                    # K <= 2^24 (per-tile byte offsets stay below 2^31)
+KMAX_PREP = (1 << 24) - 256           # prepared: (K/256) * 32 KiB < 2^31
+KMAX_EXP = 61230 * 256                # expanded: (K/256) * 35,072 < 2^31
+
+
+def big_activations(K, rows, src_rows, seed):
+    """Device X [len(src_rows)][K] whose token t is host row src_rows[t] of `rows` distinct
+    seeded rows (the oracle needs only those)."""
+    _, Xd = inputs.small_case("q4_K", rows, 1, K, seed=seed, gain=True)
+    idx = torch.tensor(src_rows, dtype=torch.int64, device=DEV)
+    return Xd, dev(Xd).index_select(0, idx)
+
+
+@pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
+def test_max_K_and_q_plane_past_2GiB(wtype):
+    """K = 2^24 (65,536 super-blocks) with M = 150 tokens and N = 5 rows: the q8_1 plane is
+    2.5 GB, so tokens 128.. start past 2^31 bytes. Each token is one of 4 distinct rows: its
+    output must match the oracle on that row, and equal tokens must agree bit for bit. The
+    K-split entry point (3 tiles, 8 pieces) is checked the same way."""
+    M, N, K = 150, 5, KMAX_RAW
+    src = [(7 * t) % 4 for t in range(M)]
+    say(f"[max K {wtype} {M}x{N}x{K}]")
+    Xh, Xd = big_activations(K, 4, src, seed=21)
+    Wh, _ = inputs.small_case(wtype, 1, N, K, seed=22)
+    w = dev(Wh.reshape(-1))
+    xq = B.quantize_q8_1(Xd)
+    plain = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
+    sk = B.mmq_q4K_q8_sk if wtype == "q4_K" else B.mmq_q6K_q8_sk
+    y = plain(w, xq, M, N, K)
+    ys = sk(w, xq, M, N, K)
+    torch.cuda.synchronize()
+    del Xd, xq
+    ref = O.mmq(wtype, Wh, Xh)                      # [4][N]
+    for tag, g in (("plain", y.cpu().numpy()), ("split", ys.cpu().numpy())):
+        for r in range(4):
+            toks = [t for t in range(M) if src[t] == r]
+            assert all(np.array_equal(g[toks[0]], g[t]) for t in toks)
+        check_out(g, ref[src], f"max K {wtype} {tag}")
+
+
+@pytest.mark.parametrize("form", ["q6K_prep", "q6K_exp"])
+def test_max_K_prepared_and_expanded(form):
+    """The largest K each repacked q6_K layout accepts (its per-tile record range just under
+    2^31 bytes), M = 3, N = 5."""
+    K = KMAX_PREP if form == "q6K_prep" else KMAX_EXP
+    M, N = 3, 5
+    say(f"[max K {form} {M}x{N}x{K}]")
+    Wh, Xh = inputs.small_case("q6_K", M, N, K, seed=23, gain=True)
+    w = dev(Wh.reshape(-1))
+    xq = B.quantize_q8_1(dev(Xh))
+    if form == "q6K_prep":
+        assert B.q6K_prep_bytes(N, K + 256) == 0
+        y = B.mmq_q6K_prep_q8(B.q6K_prepare(w, N, K), xq, M, N, K)
+    else:
+        assert B.q6K_exp_bytes(N, K + 256) == 0
+        y = B.mmq_q6K_exp_q8(B.q6K_expand(w, N, K), xq, M, N, K)
+    torch.cuda.synchronize()
+    check_out(y.cpu().numpy(), O.mmq("q6_K", Wh, Xh), f"max K {form}")
+
+
+def test_degenerate_zero_blocks():
+    """Zero activations (amax = 0: d = 0, q = 0, ssum = 0), all-zero tokens, zero weight
+    super-blocks (d = dmin = 0) and zero scales: exact zeros where the definition gives zero,
+    the oracle elsewhere, for every weight form."""
+    M, N, K = 70, 130, 1024
+    say("[degenerate zero blocks]")
+    for wtype in ("q4_K", "q6_K"):
+        W, X = inputs.small_case(wtype, M, N, K, seed=24, gain=True)
+        X = X.copy()
+        X[5] = 0.0                                   # a whole token of zeros
+        X[9, 64:96] = 0.0                            # one zero chunk
+        X[:, 512:544] = 0.0                          # a zero chunk in every token
+        W = W.copy()
+        bpb = 144 if wtype == "q4_K" else 210
+        Wb = W.reshape(N, K // 256, bpb)
+        Wb[3, :, :] = 0                              # a whole row of zero blocks
+        Wb[17, 2, :] = 0                             # one zero super-block
+        W = Wb.reshape(N, -1)
+        r = O.mmq(wtype, W, X)
+        assert np.all(r[5] == 0) and np.all(r[:, 3] == 0)
+        xq, _ = gpu_quantize(X)
+        w = dev(W.reshape(-1))
+        outs = [("raw", (B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8)(w, xq, M, N, K))]
+        if wtype == "q6_K":
+            outs.append(("prep", B.mmq_q6K_prep_q8(B.q6K_prepare(w, N, K), xq, M, N, K)))
+            outs.append(("exp", B.mmq_q6K_exp_q8(B.q6K_expand(w, N, K), xq, M, N, K)))
+        torch.cuda.synchronize()
+        for tag, y in outs:
+            g = y.cpu().numpy()
+            assert np.all(g[5] == 0) and np.all(g[:, 3] == 0), f"{wtype} {tag}"
+            check_out(g, r, f"zeros {wtype} {tag}")
+
+
 def test_closed_form_scale_path_on_gpu():
     """All nib = 1, sc = 1, d = 1, X = 1: Y = K * 0.99993896484375 exactly (golden)."""
     K = 1024
