@@ -477,19 +477,26 @@ def test_closed_form_scale_path_on_gpu():
     assert np.all(y == np.float32(1023.9375))
 
 
-def test_stack_sampled_rows():
-    """7B-style stack (M = 1024): each of the 4 distinct GEMM shapes of layer 0 and a later
-    layer, full GPU GEMM, 16 sampled weight rows checked against the oracle."""
-    rng = np.random.default_rng(17)
-    for layer in (0, 31):
-        for idx in (0, 2, 4, 6):           # q (q4_K 4096^2), v (q6_K 4096^2), gate, down
-            name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
-            X = inputs.make_stack_input(layer, idx)
-            say(f"[stack layer {layer} {name} {wtype} {X.shape[0]}x{N}x{K}]")
-            g = gpu_mmq(wtype, W, X, N)
-            rows = np.sort(rng.choice(N, 16, replace=False))
-            r = O.mmq(wtype, W[rows], X)
-            check_out(g[:, rows], r, f"stack L{layer} {name}")
+@pytest.mark.parametrize("layer", [0, 31])
+def test_stack_layers(layer):
+    """7B-style stack (M = 1024), each of the 4 distinct GEMM shapes of a layer (q4_K q and
+    gate, q6_K v and down; q6_K also on expanded weights, the form the stack bench runs):
+    layer 0 against the oracle in full, layer 31 on 16 sampled weight rows."""
+    rng = np.random.default_rng(17 + layer)
+    for idx in (0, 2, 4, 6):               # q (q4_K 4096^2), v (q6_K 4096^2), gate, down
+        name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
+        X = inputs.make_stack_input(layer, idx)
+        say(f"[stack layer {layer} {name} {wtype} {X.shape[0]}x{N}x{K}]")
+        outs = [("", gpu_mmq(wtype, W, X, N))]
+        if wtype == "q6_K":
+            xq, _ = gpu_quantize(X)
+            y = B.mmq_q6K_exp_q8(gpu_expand(W, N, K), xq, X.shape[0], N, K)
+            torch.cuda.synchronize()
+            outs.append((" expanded", y.cpu().numpy()))
+        rows = np.arange(N) if layer == 0 else np.sort(rng.choice(N, 16, replace=False))
+        r = O.mmq(wtype, W if layer == 0 else W[rows], X)
+        for tag, g in outs:
+            check_out(g[:, rows], r, f"stack L{layer} {name}{tag}")
 
 
 def test_graph_replay_matches_eager():
