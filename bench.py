@@ -11,6 +11,7 @@ time): the first ~10-20 ms of a run are up to 10 % slower while the clock ramps 
 Other modes:
   --shards                   the N/8 shares of the 7B layer GEMMs, plain vs K-split entry
                              points (one JSON line per shape)
+  --msweep                   the 7B layer GEMM shapes at M = 16 .. 2048 tokens, likewise
 For rocprofv3 runs:
   --profile {q4K,q6K,q6Kp,q6Kx,quant}  a few launches of one kernel (q6_K raw / prepared /
                              expanded), no timing output
@@ -303,21 +304,27 @@ def profile_mode(which: str, launches: int):
     print(f"profiled {which}: {launches} launches of {wtype} {M}x{N}x{K}", flush=True)
 
 
+MSWEEP_M = (16, 64, 128, 256, 512, 1024, 2048)
+MSWEEP_SHAPES = [("q4K", 4096, 4096, "q/k/o 4096x4096 q4_K"), ("q6K_exp", 4096, 4096, "v 4096x4096 q6_K expanded"),
+                 ("q4K", 11008, 4096, "gate/up 11008x4096 q4_K"), ("q6K_exp", 4096, 11008, "down 4096x11008 q6_K expanded")]
+
 SHARD_SHAPES = [("q4K", 512, 1376, 4096, "gate/up share"), ("q4K", 512, 512, 4096, "q/k/v/o share"),
                 ("q6K", 512, 512, 11008, "down share, raw q6_K"), ("q6K_prep", 512, 512, 11008, "down share, prepared"),
                 ("q6K_exp", 512, 512, 11008, "down share, expanded"), ("q4K", 128, 4096, 4096, "short prompt")]
 
 
-def run_shards(steps: int, warmup: int):
-    """One GPU's N/8 share of each 7B layer GEMM (M = 512) and a short prompt: the plain entry
-    point against the K-split entry point (partial tiles + reduce), HIP events around `steps`
-    back-to-back calls of each. One JSON line per shape."""
+def run_shards(steps: int, warmup: int, shapes=None):
+    """One GPU's N/8 share of each 7B layer GEMM (M = 512) and a short prompt, or with
+    `shapes` any (form, M, N, K, label) list: the plain entry point against the K-split entry
+    point (partial tiles + reduce; the plain kernel when the shape needs no split): HIP events
+    around `steps` back-to-back calls, five rounds with the two alternating, median per entry.
+    One JSON line per shape."""
     import torch
     from quantized_prefill_gemm_amd import binding as B
     from quantized_prefill_gemm_amd import inputs
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    for form, M, N, K, what in SHARD_SHAPES:
+    for form, M, N, K, what in (shapes or SHARD_SHAPES):
         wtype = "q4_K" if form == "q4K" else "q6_K"
         W, X = inputs.small_case(wtype, M, N, K, seed=1)
         w = torch.from_numpy(W.reshape(-1)).to(dev)
@@ -333,19 +340,25 @@ def run_shards(steps: int, warmup: int):
                  "q6K_exp": B.mmq_q6K_exp_q8}[form]
         sk = {"q4K": B.mmq_q4K_q8_sk, "q6K": B.mmq_q6K_q8_sk, "q6K_prep": B.mmq_q6K_prep_q8_sk,
               "q6K_exp": B.mmq_q6K_exp_q8_sk}[form]
-        t = {}
-        for name, fn in (("plain", lambda: plain(w, xq, M, N, K, y, stream=stream)),
-                         ("split", lambda: sk(w, xq, M, N, K, y, ws if nws else None, stream=stream))):
+        fns = {"plain": lambda: plain(w, xq, M, N, K, y, stream=stream),
+               "split": lambda: sk(w, xq, M, N, K, y, ws if nws else None, stream=stream)}
+        for fn in fns.values():
             for _ in range(warmup):
                 fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(steps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t[name] = e0.elapsed_time(e1) / steps * 1e3
+        torch.cuda.synchronize()
+        # five rounds, the two entry points alternating (the clock ramps after a change of
+        # shape, so a single plain-then-split pass favours the second); median per entry
+        t = {name: [] for name in fns}
+        for _ in range(5):
+            for name, fn in fns.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(steps):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t[name].append(e0.elapsed_time(e1) / steps * 1e3)
+        t = {name: sorted(v)[2] for name, v in t.items()}
         macs = M * N * K
         print(json.dumps({"shard": what, "form": form, "M": M, "N": N, "K": K,
                           "pieces": nws // (4 * M * N) if nws else 1,
@@ -384,6 +397,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--shards", action="store_true",
                     help="time the N/8 shares of the 7B layer GEMMs: plain vs K-split entry points")
+    ap.add_argument("--msweep", action="store_true",
+                    help="time the 7B layer GEMM shapes over M = 16..2048 tokens: plain vs K-split entry points")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
@@ -395,9 +410,11 @@ def main():
     if a.profile:
         profile_mode(a.profile, a.launches)
         return
-    if a.shards:
-        run_shards(a.steps if a.steps != ap.get_default("steps") else 300,
-                   a.warmup if a.warmup != ap.get_default("warmup") else 100)
+    if a.shards or a.msweep:
+        shapes = None if a.shards else [(f, m, n, k, f"{what}, M={m}") for f, n, k, what in MSWEEP_SHAPES
+                                        for m in MSWEEP_M]
+        run_shards(a.steps if a.steps != ap.get_default("steps") else (300 if a.shards else 100),
+                   a.warmup if a.warmup != ap.get_default("warmup") else (100 if a.shards else 30), shapes)
         return
 
     if a.config == 5:
