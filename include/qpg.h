@@ -19,8 +19,12 @@
  *     synchronises. Buffers must stay valid until the stream reaches the work.
  *   - Shapes: M = tokens, N = output features (weight rows), K = input features.
  *     1 <= M, N; 256 <= K; K % 256 == 0; M, N, K < 2^31.
- *   - Return value: QPG_OK (0) on success, a negative QPG_E* code otherwise. On any
- *     error nothing has been enqueued. There is no fallback path.
+ *   - Return value: QPG_OK (0) on success, a negative QPG_E* code otherwise. Arguments
+ *     and the device are checked before anything is enqueued, so on QPG_EINVAL,
+ *     QPG_EALIGN and QPG_EDEVICE nothing has been. QPG_EHIP reports a failed kernel
+ *     launch; in the entry points that enqueue two kernels (mmq_q4K / mmq_q6K: quantise,
+ *     then the MMQ; the _sk entry points with a split: the MMQ, then the reduce) the first
+ *     may already be enqueued when the second fails. There is no fallback path.
  *   - The library runs on gfx950 only (QPG_EDEVICE otherwise).
  *
  * Data layouts
