@@ -58,12 +58,12 @@ constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks
 constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
 
 // LDS of one group of four waves (one K range of the tile). Stage-buffer layouts, in
-// 16-byte slots (a row pitch of 9 resp. 5 slots puts 16 consecutive tokens / rows of one
-// ds_read_b128 phase on 16 distinct bank groups, and every read address is one base
-// register plus an immediate):
-//   q8 tile: token t, granule g (k 16g..16g+15 of the half) at slot 9t + g; slot 9t + 8 is pad
-//   raw qs:  row j, granule g (qs bytes 16g.. of the half)   at slot 5j + g; slot 5j + 4 is pad
-constexpr int AQ_SLOTS = TM * 9, BQ_SLOTS = TN * 5;          // 576 and 640: 9 and 10 slabs of 64
+// 16-byte slots, rows unpadded and the granules of a row permuted so that the 16 consecutive
+// tokens / rows of one ds_read_b128 phase fall on 16 distinct 16-byte bank groups (the
+// permutation is applied by the LDS-direct loads' per-lane source offsets):
+//   q8 tile: token t, granule g (k 16g..16g+15 of the half) at slot 8t + (g ^ ((t >> 1) & 7))
+//   raw qs:  row j, granule g (qs bytes 16g.. of the half)   at slot 4j + (g ^ ((j >> 2) & 3))
+constexpr int AQ_SLOTS = TM * 8, BQ_SLOTS = TN * 4;          // 512 each: 8 slabs of 64
 struct GroupLds {
     alignas(16) uint8_t aq0[AQ_SLOTS * 16];
     alignas(16) uint8_t aq1[AQ_SLOTS * 16];
@@ -75,11 +75,9 @@ struct GroupLds {
     alignas(16) uint16_t bw[TN * 8];         // m per row and sub-block as bf16
     alignas(16) float bnd[TN];               // -dmin per row, rows in C-register order per wave
 };
-static_assert(sizeof(GroupLds) == 52736, "LDS of one group");
+static_assert(sizeof(GroupLds) == 46592, "LDS of one group");
 static_assert(4 * (AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= TM * TN * 4, "a group's stage buffers hold its partial tile");
 
-// Source offset of a pad slot: past every buffer's range, so the load writes zeros.
-constexpr unsigned PAD_OFF = 0x7F000000u;
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int& piece, int tiles_m, int total,
                                             int pieces)
@@ -152,19 +150,17 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         __builtin_amdgcn_make_buffer_rsrc((void*)(hdr + (size_t)m0 * nc), 0, rows_t * nc * 4, 0x00020000);
 
     // Per-lane source offsets of the LDS-direct loads. A slab is 64 consecutive slots
-    // (1 KiB) written by one wave instruction, lane L to slot 64*slab + L. The q8 tile has
-    // 9 slabs (wave w: slabs w, w+4, and 8 for wave 0), the raw qs 10 (wave w: w, w+4, and
-    // 8 + w for waves 0-1). Pad slots get PAD_OFF. Stage offsets are added per load.
-    const int nA = wave == 0 ? 3 : 2, nB = wave < 2 ? 3 : 2;
-    unsigned voA[3], voB[3];
+    // (1 KiB) written by one wave instruction, lane L to slot 64*slab + L; the lane fetches
+    // the granule that the permutation puts there. The q8 tile and the raw qs have 8 slabs
+    // each, wave w loads slabs w and w + 4 of both. Stage offsets are added per load.
+    unsigned voA[2], voB[2];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int sa = 64 * (i < 2 ? wave + 4 * i : 8) + lane;
-        const int t = sa / 9, ga = sa - 9 * t;
-        voA[i] = ga == 8 ? PAD_OFF : (unsigned)(t * K + 16 * ga);
-        const int sbq = 64 * (i < 2 ? wave + 4 * i : 8 + wave) + lane;
-        const int j = sbq / 5, gb = sbq - 5 * j;
-        voB[i] = gb == 4 ? PAD_OFF : (unsigned)(j * wrow + 16 + 16 * gb);
+    for (int i = 0; i < 2; ++i) {
+        const int sl = 64 * (wave + 4 * i) + lane;
+        const int t = sl >> 3, ga = (sl & 7) ^ ((t >> 1) & 7);
+        voA[i] = (unsigned)(t * K + 16 * ga);
+        const int j = sl >> 2, gb = (sl & 3) ^ ((j >> 2) & 3);
+        voB[i] = (unsigned)(j * wrow + 16 + 16 * gb);
     }
 
     // The stage offset moves the descriptors' base (scalar arithmetic) instead of every
@@ -180,9 +176,9 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         const __amdgpu_buffer_rsrc_t rWs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(wbase + ob), 0, (int)(nW - ob), 0x00020000);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            if (i < nA) lds_load16(rQs, aq + 1024 * (i < 2 ? wave + 4 * i : 8), (int)voA[i]);
-            if (i < nB) lds_load16(rWs, bq + 1024 * (i < 2 ? wave + 4 * i : 8 + wave), (int)voB[i]);
+        for (int i = 0; i < 2; ++i) {
+            lds_load16(rQs, aq + 1024 * (wave + 4 * i), (int)voA[i]);
+            lds_load16(rWs, bq + 1024 * (wave + 4 * i), (int)voB[i]);
         }
     };
 
@@ -210,9 +206,14 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
     const int wr = 32 * wave + l32;                 // weight row of this lane's A operand
-    // Lane bases of the compute-phase reads (everything else is an immediate offset):
-    const int aq_base = 144 * l32 + 16 * hg;         // token l32 (+32 tokens = +4608), k-group hg
-    const int bq_base = 80 * wr + 16 * hg;           // row wr, k-group hg
+    // Lane offsets of the compute-phase reads (the token sub-tile is an immediate, +4096):
+    // q8 granule 2 cl + hg of token l32 for each chunk cl of a stage, raw granule 2 p + hg of
+    // row wr for p = 0, 1.
+    int aq_off[4], bq_off[2];
+#pragma unroll
+    for (int cl = 0; cl < 4; ++cl) aq_off[cl] = 128 * l32 + 16 * ((2 * cl + hg) ^ ((l32 >> 1) & 7));
+#pragma unroll
+    for (int p = 0; p < 2; ++p) bq_off[p] = 64 * wr + 16 * ((2 * p + hg) ^ ((wr >> 2) & 3));
 
     // Decode one super-block's headers (held in registers by the thread that loaded them)
     // into the fold terms.
@@ -277,10 +278,10 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
             return r;
         };
         auto ld_raw = [&](int p) -> uint32x4 {
-            return *reinterpret_cast<const uint32x4*>(bq + bq_base + 32 * p);
+            return *reinterpret_cast<const uint32x4*>(bq + bq_off[p]);
         };
         auto ld_b = [&](int cl, int ts) -> int32x4 {
-            return *reinterpret_cast<const int32x4*>(aq + aq_base + 4608 * ts + 32 * cl);
+            return *reinterpret_cast<const int32x4*>(aq + aq_off[cl] + 4096 * ts);
         };
         if constexpr (!ISUMS) asm volatile("" : "+v"(magic));   // keep the constant in VGPRs
         uint32x4 raw = ld_raw(0);
