@@ -379,15 +379,17 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         hv = load_headers(sb0);
         issue_stage(sb0, 0, L.aq0, L.bq0);
     }
-    // The waits, barriers, header decode and load issue of each half run at wave priority 1
-    // and the compute at 0: a workgroup's short serial section then takes the issue slots
-    // ahead of the other workgroups' folds, so fewer of its waves idle at the barriers
-    // (1.5-2 % on the 512 x 11008 x 4096 and 1024 x 11008 x 4096 shapes).
+    // With one group per workgroup (several workgroups per CU), the waits, barriers, header
+    // decode and load issue of each half run at wave priority 1 and the compute at 0: a
+    // workgroup's short serial section then takes the issue slots ahead of the other
+    // workgroups' folds, so fewer of its waves idle at the barriers (1.5-2 % on the
+    // 512 x 11008 x 4096 and 1024 x 11008 x 4096 shapes; with three groups in one workgroup,
+    // where all waves meet at the same barriers, it measured ~1 % slower and is not used).
     for (int it = 0; it < iters; ++it) {
         const bool act = it < cnt, more = it + 1 < cnt;
         const int sb = sb0 + it;
         // ---- first half: wait for (sb, 0) and the headers of sb, decode the headers
-        __builtin_amdgcn_s_setprio(1);
+        if constexpr (KS == 1) __builtin_amdgcn_s_setprio(1);
         wait_vmem();
         __syncthreads();                    // stage (sb,0) visible; (sb-1,1) and its min term done
         if constexpr (!ISUMS)
@@ -395,15 +397,15 @@ __global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_k
         __syncthreads();                    // fold terms of sb visible
         if (more) hv = load_headers(sb + 1);
         if (act) issue_stage(sb, 1, L.aq1, L.bq1);
-        __builtin_amdgcn_s_setprio(0);
+        if constexpr (KS == 1) __builtin_amdgcn_s_setprio(0);
         if (act) compute_stage(sb, 0, L.aq0, L.bq0);
 
         // ---- second half
-        __builtin_amdgcn_s_setprio(1);
+        if constexpr (KS == 1) __builtin_amdgcn_s_setprio(1);
         wait_vmem();
         __syncthreads();                    // stage (sb,1) visible; buffer 0 free
         if (more) issue_stage(sb + 1, 0, L.aq0, L.bq0);
-        __builtin_amdgcn_s_setprio(0);
+        if constexpr (KS == 1) __builtin_amdgcn_s_setprio(0);
         if (act) {
             compute_stage(sb, 1, L.aq1, L.bq1);
             if constexpr (!ISUMS) min_term();
