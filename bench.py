@@ -26,6 +26,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -76,7 +78,17 @@ def setup(cfg: int):
     return B, wtype, M, N, K, W, X, w, x, y, ws
 
 
+ROUNDS = 5
+
+
 def run_gpu(cfg: int, steps: int, warmup: int, q6: str = "raw"):
+    """Warm-up steps, then exactly `steps` timed steps (the line's value). Afterwards, outside
+    the timed region, ROUNDS rounds that alternate `steps` steps, `steps` MMQ launches alone
+    and `steps` quantize launches alone, each bracketed by HIP events on the launch stream,
+    with the shader clock read right after each round: the per-kernel figures are the
+    medians of those rounds, taken under the same clock as the step figure they are
+    compared with."""
+    import statistics
     import torch
     B, wtype, M, N, K, W, X, w, x, y, ws = setup(cfg)
     mmq_q8 = B.mmq_q4K_q8 if wtype == "q4_K" else B.mmq_q6K_q8
@@ -113,24 +125,74 @@ def run_gpu(cfg: int, steps: int, warmup: int, q6: str = "raw"):
     t0 = time.perf_counter()
     step_ms = bracketed(step, steps)
     wall = time.perf_counter() - t0
-    # per-kernel averages, the same launches back to back, right after the timed steps
-    mmq_ms = bracketed(lambda: mmq_q8(w, ws, M, N, K, y, stream=stream), steps)
-    quant_ms = bracketed(lambda: B.quantize_q8_1(x, ws, stream=stream), steps)
+    rounds = {"step": [], "mmq": [], "quant": [], "clock_ghz": []}
+    clock = ClockProbe()
+    for _ in range(ROUNDS):
+        rounds["step"].append(bracketed(step, steps))
+        rounds["mmq"].append(bracketed(lambda: mmq_q8(w, ws, M, N, K, y, stream=stream), steps))
+        rounds["quant"].append(bracketed(lambda: B.quantize_q8_1(x, ws, stream=stream), steps))
+        rounds["clock_ghz"].append(clock.read())
+    med = {k: statistics.median(v) for k, v in rounds.items()}
     return dict(wtype=wtype, M=M, N=N, K=K, W=W, X=X, wall_s=wall, step_ms=step_ms,
-                quant_ms=quant_ms, mmq_ms=mmq_ms)
+                quant_ms=med["quant"], mmq_ms=med["mmq"], step_rounds_ms=med["step"],
+                clock_ghz=med["clock_ghz"], rounds=rounds)
+
+
+class ClockProbe:
+    """Shader clock right now: a short run of libqpg_calib.so's matrix-core chains on every CU
+    (s_memtime ticks over the 100 MHz s_memrealtime ticks of the same loop, median over the
+    workgroups). ~20 us, so it reads the clock the preceding work left the device at."""
+
+    def __init__(self, blocks: int = 256, iters: int = 100):
+        import ctypes
+        import torch
+        self.lib = ctypes.CDLL(os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so"))
+        self.lib.qpg_calib_mfma_i8.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.qpg_calib_mfma_i8.restype = ctypes.c_int
+        self.blocks, self.iters = blocks, iters
+        self.out = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda:0")
+        self.sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def read(self) -> float:
+        import ctypes
+        import statistics
+        import torch
+        if self.lib.qpg_calib_mfma_i8(self.blocks, self.iters, ctypes.c_void_p(self.out.data_ptr()), self.sp) != 0:
+            raise RuntimeError("qpg_calib_mfma_i8 failed")
+        torch.cuda.synchronize()
+        v = self.out.view(self.blocks, 4).cpu().numpy()
+        return statistics.median(t / (r / 100e6) for t, r in zip(v[:, 0], v[:, 1]) if r > 0) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wtype, W, X):
+    """The oracle (untuned) on the full workload: one warm run, then the median of three."""
+    import statistics
     from oracle import oracle as O
     nth = O.default_threads()
     M, K = X.shape
     N = W.shape[0]
-    t0 = time.perf_counter()
-    O.mmq(wtype, W, X, nthreads=nth)
-    dt = time.perf_counter() - t0
+    O.mmq(wtype, W, X, nthreads=nth)                 # warm: page-in, thread start-up
+    runs = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.mmq(wtype, W, X, nthreads=nth)
+        runs.append(time.perf_counter() - t0)
+    dt = statistics.median(runs)
     return {"value": M * N * K / dt / 1e12, "unit": "TMAC/s", "cores": nth, "kind": "oracle",
-            "sample": f"full workload {M}x{N}x{K} {wtype}, one run: quantize_q8_1 + exact int32 sums + fp64 fold, "
-                      f"{dt:.2f} s wall on {nth} threads"}
+            "cpu": cpu_model(),
+            "sample": f"full workload {M}x{N}x{K} {wtype}: quantize_q8_1 + exact int32 sums + fp64 fold; "
+                      f"median of 3 runs after one warm run ({', '.join(f'{r:.2f}' for r in runs)} s) "
+                      f"on {nth} threads"}
 
 
 def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
@@ -165,76 +227,89 @@ def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
             "kernel": "v_mfma_i32_32x32x32_i8 chains, 2 waves per SIMD", "seconds": round(secs, 5)}
 
 
-def run_stack(steps: int, warmup: int, q6: str):
-    """Config 5: the 32-layer 7B-shaped stack at M = 1024, each of the 7 GEMMs of a layer
-    preceded by its quantize_q8_1: 448 launches per pass, timed both as one HIP graph (torch's
-    graph API over the library's own launches) replayed, and launched eagerly. Weights: the seeded per-layer
-    generator (4.15 GB of q4_K / q6_K blocks resident in HBM); activations: one seeded input
-    per matrix position, reused by every layer."""
+STEP_MODES = {0: "mfma_only", 1: "fold_only", 2: "kernel_step", 3: "mfma_and_independent_fold"}
+
+
+def measured_step_ceiling(waves=(2, 3, 4), iters: int = 4000):
+    """The q4_K kernel's compute step alone (libqpg_calib.so qpg_calib_step: one
+    v_mfma_i32_32x32x32_i8 issued a step ahead plus the 32 fold FMAs of the previous result,
+    per wave and step; no memory traffic, barriers, decode or min term), at 2-4 waves per
+    SIMD. Each mode is timed with HIP events around one launch; the rate is counted in the
+    int8 ops of the MFMAs (2 per MAC) the steps stand for, also for the fold-only mode.
+    Returns the rate of the kernel's step at its production occupancy (3 waves per SIMD) as
+    the ceiling of its arithmetic, plus every mode and occupancy."""
+    import ctypes
     import torch
-    from quantized_prefill_gemm_amd import binding as B
+    lib = ctypes.CDLL(os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so"))
+    lib.qpg_calib_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.qpg_calib_step.restype = ctypes.c_int
+    lib.qpg_calib_step_blocks.argtypes = [ctypes.c_int]
+    lib.qpg_calib_step_blocks.restype = ctypes.c_int64
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    table = {}
+    for w in waves:
+        nb = lib.qpg_calib_step_blocks(w)
+        out = torch.zeros(nb * 4, dtype=torch.int64, device="cuda:0")
+        row = {}
+        for mode, name in STEP_MODES.items():
+            if lib.qpg_calib_step(mode, w, 50, ctypes.c_void_p(out.data_ptr()), sp) != 0:   # warm
+                raise RuntimeError("qpg_calib_step failed")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            rc = lib.qpg_calib_step(mode, w, iters, ctypes.c_void_p(out.data_ptr()), sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError("qpg_calib_step failed")
+            secs = e0.elapsed_time(e1) * 1e-3
+            v = out.view(nb, 4).cpu().numpy()
+            ghz = float(np.median(v[:, 0] / (v[:, 1] / 100e6))) / 1e9
+            steps_per_simd = iters * 8 * w
+            row[name] = {"tops": round(2 * nb * 4 * iters * 8 * 32768 / secs / 1e12, 1),
+                         "ns_per_step_per_simd": round(secs * 1e9 / steps_per_simd, 2),
+                         "clock_ghz": round(ghz, 3)}
+        table[f"{w}_waves_per_simd"] = row
+    ks = table["3_waves_per_simd"]
+    m0, m1, m2, m3 = (ks[STEP_MODES[i]]["ns_per_step_per_simd"] for i in range(4))
+    return {"value": ks["kernel_step"]["tops"], "unit": "TOP/s",
+            "frac_of_peak": round(ks["kernel_step"]["tops"] / PEAK_INT8_TOPS, 4),
+            "clock_ghz": ks["kernel_step"]["clock_ghz"],
+            "what": "q4_K compute step alone at 3 waves per SIMD (1 MFMA 32x32x32 i8 + 32 fold FMAs per "
+                    "wave and step, no memory, barriers, decode or min term)",
+            "overlap": {"mfma_ns": m0, "fold_ns": m1, "sum_ns": round(m0 + m1, 2), "max_ns": max(m0, m1),
+                        "both_independent_ns": m3, "kernel_step_ns": m2},
+            "modes": table}
+
+
+def run_stack(steps: int, warmup: int, q6: str):
+    """Config 5: the 32-layer 7B-shaped stack at M = 1024 (quantized_prefill_gemm_amd.stack),
+    each of the 7 GEMMs of a layer preceded by its quantize_q8_1 (448 launches per pass), and
+    with one quantize per distinct input (4 per layer), and the GEMMs alone; each timed both as
+    one HIP graph replayed and launched eagerly. Weights: the seeded per-layer generator
+    (4.15 GB of q4_K / q6_K blocks resident in HBM); activations: one seeded input per
+    distinct input position, reused by every layer."""
+    import torch
     from quantized_prefill_gemm_amd import inputs
+    from quantized_prefill_gemm_amd.stack import MODES, SOURCES, Stack
     M, L = inputs.STACK_M, inputs.STACK_LAYERS
     dev = torch.device("cuda:0")
-    mats = []
+    weights = []
     for layer in range(L):
-        for idx in range(len(inputs.STACK_LAYER)):
-            name, wtype, N, K, W = inputs.make_stack_matrix(layer, idx)
-            w = torch.from_numpy(W.reshape(-1)).to(dev)
-            if wtype == "q6_K" and q6 == "prepared":
-                w = B.q6K_prepare(w, N, K)
-            elif wtype == "q6_K" and q6 == "expanded":
-                w = B.q6K_expand(w, N, K)
-            mats.append((idx, wtype, N, K, w))
-        torch.cuda.synchronize()
+        weights.append([torch.from_numpy(inputs.make_stack_matrix(layer, idx)[4].reshape(-1)).to(dev)
+                        for idx in range(len(inputs.STACK_LAYER))])
         if layer % 8 == 7:
             print(f"stack weights: {layer + 1}/{L} layers resident", file=sys.stderr, flush=True)
-    xs, xqs, ys = {}, {}, {}
-    for idx, (name, wtype, N, K) in enumerate(inputs.STACK_LAYER):
-        xs[idx] = torch.from_numpy(inputs.make_stack_input(0, idx)).to(dev)
-        xqs[idx] = torch.empty(B.q8_1_bytes(M, K), dtype=torch.uint8, device=dev)
-        ys[idx] = torch.empty((M, N), dtype=torch.float32, device=dev)
-    # q, k, v read the same hidden state and gate, up the same normed state: with
-    # quantize sharing, one quantize serves each group (4 per layer instead of 7)
-    share_src = {0: 0, 1: 0, 2: 0, 3: 3, 4: 4, 5: 4, 6: 6}
-
-    def mmq(idx, wtype, N, K, w, xq):
-        if wtype == "q4_K":
-            B.mmq_q4K_q8(w, xq, M, N, K, ys[idx])
-        elif q6 == "prepared":
-            B.mmq_q6K_prep_q8(w, xq, M, N, K, ys[idx])
-        elif q6 == "expanded":
-            B.mmq_q6K_exp_q8(w, xq, M, N, K, ys[idx])
-        else:
-            B.mmq_q6K_q8(w, xq, M, N, K, ys[idx])
-
-    def pass_(mode):
-        for idx, wtype, N, K, w in mats:
-            if mode == "all":
-                B.quantize_q8_1(xs[idx], xqs[idx])
-                mmq(idx, wtype, N, K, w, xqs[idx])
-            elif mode == "shared":
-                src = share_src[idx]
-                if src == idx:
-                    B.quantize_q8_1(xs[idx], xqs[idx])
-                mmq(idx, wtype, N, K, w, xqs[src])
-            else:                                   # "gemm": the GEMMs alone
-                mmq(idx, wtype, N, K, w, xqs[idx])
-
-    for idx in xs:
-        B.quantize_q8_1(xs[idx], xqs[idx])
+    st = Stack(weights, M, q6=q6)
+    del weights
+    for src in SOURCES:
+        st.set_input(0, src, torch.from_numpy(inputs.make_stack_input(0, src)).to(dev))
+    st.run("all")
     torch.cuda.synchronize()
     res = {}
-    for mode in ("all", "shared", "gemm"):
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            pass_(mode)                              # eager warm-up on the capture stream
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g):
-            pass_(mode)
+    for mode in MODES:
+        g = st.capture(mode)
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
@@ -250,20 +325,19 @@ def run_stack(steps: int, warmup: int, q6: str):
         # the same pass launched eagerly (the host stays ahead of the GPU: ~15 us per launch
         # against ~60 us per kernel), timed as a whole
         for _ in range(warmup):
-            pass_(mode)
+            st.run(mode)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(steps):
-            pass_(mode)
+            st.run(mode)
         e1.record()
         torch.cuda.synchronize()
         res[mode + "_eager"] = e0.elapsed_time(e1) / steps
         res[mode] = min(res[mode + "_graph"], res[mode + "_eager"])
         print(f"stack '{mode}': graph median {res[mode + '_graph']:.3f} ms, eager mean "
               f"{res[mode + '_eager']:.3f} ms per pass", file=sys.stderr, flush=True)
-    macs = M * L * sum(N * K for _, _, N, K in inputs.STACK_LAYER)
-    return macs, res
+    return st.macs(), res
 
 
 def stack_cpu_baseline():
@@ -472,29 +546,44 @@ def main():
                                   .get(q6, "") if r["wtype"] == "q6_K" else ""),
                    "M": M, "N": N, "K": K, "weights": r["wtype"]},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 5), "traffic": traffic,
+                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_TOPS, 5), "traffic": traffic,
                      "kernel": f"mmq_{r['wtype'].replace('_', '')}{'_exp' if q6 == 'expanded' and r['wtype'] == 'q6_K' else ''}_kernel",
                      "avg_us": round(r["mmq_ms"] * 1e3, 3),
-                     "note": "int8 ops counted as 2 per MAC, as in the 5.0 POP/s dense peak"},
+                     "note": "int8 ops counted as 2 per MAC, as in the 5.0 POP/s dense int8 peak"},
         "kernels_us": {"quantize_q8_1": round(r["quant_ms"] * 1e3, 3), "mmq": round(r["mmq_ms"] * 1e3, 3),
-                       "timing": "HIP events on the launch stream around K back-to-back launches of "
-                                 "each kernel, right after the K timed steps"},
+                       "step": round(r["step_rounds_ms"] * 1e3, 3),
+                       "timing": f"after the K timed steps, {ROUNDS} rounds alternating K steps, K MMQ "
+                                 "launches alone and K quantize launches alone, HIP events on the launch "
+                                 "stream around each; medians",
+                       "rounds_us": {k: [round(t * 1e3, 3) for t in v] for k, v in r["rounds"].items()
+                                     if k != "clock_ghz"}},
+        "clock_ghz": {"median": round(r["clock_ghz"], 3), "rounds": [round(c, 3) for c in r["rounds"]["clock_ghz"]],
+                      "how": "shader clock read right after each round (s_memtime over s_memrealtime)"},
         "mmq_tmacs": round(macs / mmq_s / 1e12, 3),
         "mmq_hbm_gbs_algorithmic": round(algorithmic_bytes(M, N, K, 144 if r["wtype"] == "q4_K" else
                                                            {"raw": 210, "prepared": 256, "expanded": 548}[q6])
                                          / mmq_s / 1e9, 1),
         "wall_s": round(r["wall_s"], 4),
     }
-    # The fold (2 f32 FMAs per output and 32-chunk for q4_K, 4 for q6_K, 3 for expanded q6_K) runs on the VALU, which
-    # the matrix core does not overlap on this device; its share against the f32 vector peak.
+    # consistency of the line: the MMQ alone cannot take longer than quantize + MMQ measured in
+    # the same rounds; a line where it does is flagged, not silently printed
+    out["self_check"] = {"mmq_us_below_step_us": r["mmq_ms"] < r["step_rounds_ms"],
+                         "quant_plus_mmq_over_step": round((r["mmq_ms"] + r["quant_ms"]) / r["step_rounds_ms"], 4)}
+    # The fold (2 f32 FMAs per output and 32-chunk for q4_K, 4 for q6_K, 3 for expanded q6_K) on the VALU, against
+    # the f32 vector peak.
     fold_fma = M * N * (K // 32) * (2 if r["wtype"] == "q4_K" else 3 if q6 == "expanded" else 4)
     fold_tflops = 2 * fold_fma / mmq_s / 1e12
     out["fold_valu"] = {"achieved": round(fold_tflops, 2), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(fold_tflops / PEAK_F32_VALU_TFLOPS, 4),
-                        "mfma_plus_fold_frac": round(achieved / PEAK_INT8_TOPS + fold_tflops / PEAK_F32_VALU_TFLOPS, 4)}
+                        "frac": round(fold_tflops / PEAK_F32_VALU_TFLOPS, 4)}
     pk = measured_mfma_peak()
     pk["achieved_frac_of_measured"] = round(achieved / pk["value"], 5)
     out["mfma_peak_measured"] = pk
+    if r["wtype"] == "q4_K":
+        ceil = measured_step_ceiling()
+        ceil["achieved_frac_of_ceiling"] = round(achieved / ceil["value"], 4)
+        out["roofline"]["ceiling"] = ceil["value"]
+        out["roofline"]["ceiling_frac"] = ceil["achieved_frac_of_ceiling"]
+        out["step_ceiling"] = ceil
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(r["wtype"], r["W"], r["X"])
     print(json.dumps(out), flush=True)

@@ -1,4 +1,5 @@
-/* libqpg_calib.so: measurement helper for the k-quant MMQ library (not part of the GEMM path).
+/* libqpg_calib.so: measurement and probe helpers for the k-quant MMQ library (not part of the
+ * GEMM path).
  *
  * The int8 MFMA roofline of the MMQ kernels is priced against the published dense peak of
  * the device; this library measures the peak the matrix cores actually reach, and the
@@ -26,6 +27,34 @@ extern "C" {
  * -2 (QPG_EALIGN), -3 (QPG_EHIP: launch error) or -4 (QPG_EDEVICE: current device is not
  * gfx950). Nothing is allocated. */
 int qpg_calib_mfma_i8(int64_t blocks, int64_t iters, uint64_t* out, void* stream);
+
+/* Compute-step ceiling of the q4_K MMQ kernel: its inner step with no memory traffic, no
+ * barriers, no header decode and no min term. Per wave and step one v_mfma_i32_32x32x32_i8
+ * onto the 1.5*2^23 constant, issued one step ahead, and the fold of the previous result
+ * (e = fma(F, da, -1.5*2^23*da), y = fma(e, dsv, y) on its 16 registers: 32 f32 FMAs).
+ *   mode 0: the MFMAs alone; 1: the fold alone (opaque operands); 2: the kernel's step;
+ *   3: MFMAs and a fold that does not depend on them (do the two units run concurrently).
+ * waves_per_simd in {2, 3, 4}: the launch holds exactly that many waves on every SIMD
+ * (qpg_calib_step_blocks(w) workgroups of four waves, LDS sized so that w fit a CU).
+ * Every wave runs iters x 8 steps. out: device pointer to qpg_calib_step_blocks(w) * 4
+ * uint64 values, 8-byte aligned, owned by the caller, written as for qpg_calib_mfma_i8.
+ * Asynchronous on `stream`. Returns 0, -1 (bad mode, w, iters or null out), -2 (alignment),
+ * -3 (launch error) or -4 (not gfx950). Nothing is allocated. */
+int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream);
+
+/* Workgroups qpg_calib_step launches for waves_per_simd (CUs x w), 0 if w is outside
+ * {2, 3, 4} or the current device is not gfx950. */
+int64_t qpg_calib_step_blocks(int waves_per_simd);
+
+/* Matrix-instruction layout probe: one wave executes one instruction, lane l's source
+ * registers read from a / b / c at lane-major offsets and its result registers written to d.
+ *   kind 0: v_mfma_i32_32x32x32_i8   a, b: 64 x 16 bytes (int8x16), c, d: 64 x 16 int32
+ *   kind 1: v_mfma_i32_32x32x16_i8   a, b: 64 x 8 bytes (int8x8),   c, d: 64 x 16 int32
+ *   kind 2: v_mfma_f32_32x32x16_bf16 a, b: 64 x 8 bf16,             c, d: 64 x 16 f32
+ * Device pointers owned by the caller; a and b 16-byte aligned (8 for kind 1), c and d 16.
+ * Asynchronous on `stream`. Returns 0, -1 (null pointer or bad kind), -2 (alignment),
+ * -3 (launch error) or -4 (not gfx950). */
+int qpg_probe_mfma(int kind, const void* a, const void* b, const void* c, void* d, void* stream);
 
 #ifdef __cplusplus
 }

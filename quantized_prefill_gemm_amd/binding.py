@@ -96,6 +96,21 @@ def _dev(t: torch.Tensor, dtype, name: str):
         raise QPGError(QPG_EINVAL, f"{name} must be contiguous")
 
 
+def _same_device(t: torch.Tensor, ref: torch.Tensor, name: str):
+    if t.device != ref.device:
+        raise QPGError(QPG_EINVAL, f"{name} is on {t.device}, the inputs on {ref.device}")
+
+
+def _out(t: torch.Tensor, dtype, name: str, need: int, ref: torch.Tensor):
+    """A caller-supplied output: device tensor of dtype, contiguous, on ref's device and
+    holding at least `need` elements (the C ABI takes no output size, so an undersized
+    buffer would be written past its end)."""
+    _dev(t, dtype, name)
+    _same_device(t, ref, name)
+    if t.numel() < need:
+        raise QPGError(QPG_EINVAL, f"{name} holds {t.numel()} elements, {need} needed")
+
+
 def q8_1_bytes(M: int, K: int) -> int:
     return int(lib().qpg_q8_1_bytes(M, K))
 
@@ -107,9 +122,7 @@ def quantize_q8_1(x: torch.Tensor, xq: torch.Tensor | None = None, stream=None) 
     nbytes = q8_1_bytes(M, K)
     if xq is None:
         xq = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
-    _dev(xq, torch.uint8, "xq")
-    if xq.numel() < nbytes:
-        raise QPGError(QPG_EINVAL, "xq too small")
+    _out(xq, torch.uint8, "xq", nbytes, x)
     _check(lib().quantize_q8_1(_ptr(x), _ptr(xq), M, K, _stream(stream)), "quantize_q8_1")
     return xq
 
@@ -124,14 +137,13 @@ def _mmq(which: str, w, x, N, y, xq_ws, stream):
     _dev(x, torch.float32, "x")
     M, K = x.shape
     _wcheck(w, N, K, 144 if which == "q4K" else 210)
+    _same_device(w, x, "w")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    _dev(y, torch.float32, "y")
+    _out(y, torch.float32, "y", M * N, x)
     if xq_ws is None:
         xq_ws = torch.empty(max(q8_1_bytes(M, K), 1), dtype=torch.uint8, device=x.device)
-    _dev(xq_ws, torch.uint8, "xq_ws")
-    if xq_ws.numel() < q8_1_bytes(M, K):
-        raise QPGError(QPG_EINVAL, "xq_ws too small")
+    _out(xq_ws, torch.uint8, "xq_ws", q8_1_bytes(M, K), x)
     fn = lib().mmq_q4K if which == "q4K" else lib().mmq_q6K
     _check(fn(_ptr(w), _ptr(x), _ptr(y), M, N, K, _ptr(xq_ws), _stream(stream)), "mmq_" + which)
     return y
@@ -151,16 +163,17 @@ def _mmq_q8(which: str, w, xq, M, N, K, out, stream, isums: bool):
     if xq.numel() < q8_1_bytes(M, K):
         raise QPGError(QPG_EINVAL, "xq too small")
     _wcheck(w, N, K, 144 if which == "q4K" else 210)
+    _same_device(w, xq, "w")
     if isums:
         per = 32 if which == "q4K" else 16
         if out is None:
             out = torch.empty((M, N, K // per), dtype=torch.int32, device=xq.device)
-        _dev(out, torch.int32, "s")
+        _out(out, torch.int32, "s", M * N * (K // per), xq)
         fn = lib().mmq_q4K_isums if which == "q4K" else lib().mmq_q6K_isums
     else:
         if out is None:
             out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-        _dev(out, torch.float32, "y")
+        _out(out, torch.float32, "y", M * N, xq)
         fn = lib().mmq_q4K_q8 if which == "q4K" else lib().mmq_q6K_q8
     _check(fn(_ptr(w), _ptr(xq), _ptr(out), M, N, K, _stream(stream)),
            ("mmq_%s_isums" if isums else "mmq_%s_q8") % which)
@@ -195,9 +208,7 @@ def q6K_prepare(w: torch.Tensor, N: int, K: int, wp=None, stream=None) -> torch.
         raise QPGError(QPG_EINVAL, f"unsupported shape N={N} K={K}")
     if wp is None:
         wp = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
-    _dev(wp, torch.uint8, "wp")
-    if wp.numel() < nbytes:
-        raise QPGError(QPG_EINVAL, "wp too small")
+    _out(wp, torch.uint8, "wp", nbytes, w)
     _check(lib().q6K_prepare(_ptr(w), _ptr(wp), N, K, _stream(stream)), "q6K_prepare")
     return wp
 
@@ -207,17 +218,18 @@ def _mmq_prep(wp, xq, M, N, K, out, stream, isums: bool):
     if xq.numel() < q8_1_bytes(M, K):
         raise QPGError(QPG_EINVAL, "xq too small")
     _dev(wp, torch.uint8, "wp")
+    _same_device(wp, xq, "wp")
     if wp.numel() < q6K_prep_bytes(N, K):
         raise QPGError(QPG_EINVAL, "wp too small")
     if isums:
         if out is None:
             out = torch.empty((M, N, K // 16), dtype=torch.int32, device=xq.device)
-        _dev(out, torch.int32, "s")
+        _out(out, torch.int32, "s", M * N * (K // 16), xq)
         fn = lib().mmq_q6K_prep_isums
     else:
         if out is None:
             out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-        _dev(out, torch.float32, "y")
+        _out(out, torch.float32, "y", M * N, xq)
         fn = lib().mmq_q6K_prep_q8
     _check(fn(_ptr(wp), _ptr(xq), _ptr(out), M, N, K, _stream(stream)),
            "mmq_q6K_prep_isums" if isums else "mmq_q6K_prep_q8")
@@ -244,9 +256,7 @@ def q6K_expand(w: torch.Tensor, N: int, K: int, we=None, stream=None) -> torch.T
         raise QPGError(QPG_EINVAL, f"unsupported shape N={N} K={K}")
     if we is None:
         we = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
-    _dev(we, torch.uint8, "we")
-    if we.numel() < nbytes:
-        raise QPGError(QPG_EINVAL, "we too small")
+    _out(we, torch.uint8, "we", nbytes, w)
     _check(lib().q6K_expand(_ptr(w), _ptr(we), N, K, _stream(stream)), "q6K_expand")
     return we
 
@@ -256,17 +266,18 @@ def _mmq_exp(we, xq, M, N, K, out, stream, csums: bool):
     if xq.numel() < q8_1_bytes(M, K):
         raise QPGError(QPG_EINVAL, "xq too small")
     _dev(we, torch.uint8, "we")
+    _same_device(we, xq, "we")
     if we.numel() < q6K_exp_bytes(N, K):
         raise QPGError(QPG_EINVAL, "we too small")
     if csums:
         if out is None:
             out = torch.empty((M, N, K // 32), dtype=torch.int32, device=xq.device)
-        _dev(out, torch.int32, "s")
+        _out(out, torch.int32, "s", M * N * (K // 32), xq)
         fn = lib().mmq_q6K_exp_csums
     else:
         if out is None:
             out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-        _dev(out, torch.float32, "y")
+        _out(out, torch.float32, "y", M * N, xq)
         fn = lib().mmq_q6K_exp_q8
     _check(fn(_ptr(we), _ptr(xq), _ptr(out), M, N, K, _stream(stream)),
            "mmq_q6K_exp_csums" if csums else "mmq_q6K_exp_q8")
@@ -303,14 +314,15 @@ def _mmq_sk(form: str, w, xq, M, N, K, y, ws, stream):
         need = q6K_prep_bytes(N, K) if form == "q6K_prep" else q6K_exp_bytes(N, K)
         if w.numel() < need:
             raise QPGError(QPG_EINVAL, "w too small")
+    _same_device(w, xq, "w")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
-    _dev(y, torch.float32, "y")
+    _out(y, torch.float32, "y", M * N, xq)
     nws = mmq_sk_bytes(M, N, K, form)
     if ws is None and nws:
         ws = torch.empty(nws // 4, dtype=torch.float32, device=xq.device)
     if ws is not None:
-        _dev(ws, torch.float32, "ws")
+        _out(ws, torch.float32, "ws", nws // 4, xq)
     wsb = 0 if ws is None else ws.numel() * 4
     _check(getattr(lib(), _SK_FN[form])(_ptr(w), _ptr(xq), _ptr(y), M, N, K, _ptr(ws), wsb, _stream(stream)),
            _SK_FN[form])

@@ -1,0 +1,163 @@
+// Compute-step ceiling probe for gfx950 (declared in include/qpg_calib.h).
+//
+// The q4_K MMQ kernel's inner step, with nothing else: per wave and step, one
+// v_mfma_i32_32x32x32_i8 onto the bits of 1.5*2^23 (issued one step ahead of its use), then
+// the fold of the previous step's 16 accumulator registers -- e = fma(F, da, -1.5*2^23*da),
+// y = fma(e, dsv, y): 32 f32 FMAs -- into one of two token sub-tiles' accumulators. No
+// global or LDS traffic, no barriers, no header decode, no min term: the rate this runs at
+// is the ceiling of the kernel's arithmetic at a given number of waves per SIMD.
+//
+// Variants isolate the two units:
+//   mode 0  the MFMAs alone (same issue pattern, results only kept live),
+//   mode 1  the fold alone (its F operands made opaque per step instead of MFMA results),
+//   mode 2  the kernel's step: MFMA one step ahead, fold of the previous result,
+//   mode 3  MFMA and fold with no dependency between them (the fold reads opaque values):
+//           shows whether the matrix core and the VALU run concurrently at all.
+// Occupancy is fixed by the launch: 256 * W workgroups of four waves, each holding
+// 160 KiB / W of LDS (touched once), so every CU runs exactly W workgroups and each SIMD
+// W waves.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../../include/qpg_calib.h"
+
+namespace {
+
+typedef int int32x4 __attribute__((ext_vector_type(4)));
+typedef int int32x16 __attribute__((ext_vector_type(16)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMagicBits = 0x4B400000;          // bits of the f32 value 1.5 * 2^23
+constexpr float kMagic = 12582912.0f;
+
+template <int W>
+struct LdsCap {
+    static constexpr int bytes = (160 * 1024 / W) & ~1023;
+};
+
+template <int MODE, int W>
+__global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
+{
+    __shared__ int cap[LdsCap<W>::bytes / 4];
+    const int tx = (int)threadIdx.x, lane = tx & 63;
+    cap[tx] = tx;
+    int32x4 a = {lane * 0x01010101, 0x0F0E0D0C, 0x07060504 ^ lane, (int)blockIdx.x};
+    const int32x4 b = {0x7F017F01, tx * 3, 0x10203040, -tx};
+    int32x16 magic;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
+    // fold terms: da is an exact f16 value, c0 = -1.5*2^23*da exact, dsv per register
+    const float da = 0.0078125f * (float)(1 + (lane & 7)), c0 = -kMagic * da;
+    float dsv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsv[r] = 0.001f * (float)(r + 1 + (lane & 3));
+    floatx16 y[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) y[t][r] = 0.0f;
+    int32x16 F[2];
+    F[0] = magic;
+    F[1] = magic;
+    F[0][0] += lane;
+    int32x16 opaque = F[0];
+
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    if constexpr (MODE != 1) F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            asm volatile("" : "+v"(magic));
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (MODE != 1) {
+                F[(k + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
+                if constexpr (MODE == 0 || MODE == 3) asm volatile("" : : "v"(F[(k + 1) & 1]));
+            }
+            if constexpr (MODE != 0) {
+                int32x16 Fk;
+                if constexpr (MODE == 2) {
+                    Fk = F[k & 1];
+                } else {
+                    asm volatile("" : "+v"(opaque));       // a new, unknown value every step
+                    Fk = opaque;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float e = fmaf(__int_as_float(Fk[r]), da, c0);
+                    y[k & 1][r] = fmaf(e, dsv[r], y[k & 1][r]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        a[0] += 1;
+    }
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    float s = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += y[0][r] + y[1][r];
+    __syncthreads();
+    const int si = __float_as_int(s) ^ F[0][lane & 15] ^ F[1][3] ^ cap[(tx * 7) & 255];
+    if (tx == 0) {
+        out[4 * blockIdx.x + 0] = t1 - t0;
+        out[4 * blockIdx.x + 1] = r1 - r0;
+        out[4 * blockIdx.x + 2] = (uint64_t)(uint32_t)si;
+        out[4 * blockIdx.x + 3] = 0;
+    }
+}
+
+int check_device(int* cus)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -4;
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return -4;
+    const char* n = p.gcnArchName;
+    if (!(n[0] == 'g' && n[1] == 'f' && n[2] == 'x' && n[3] == '9' && n[4] == '5' && n[5] == '0' &&
+          (n[6] == 0 || n[6] == ':')))
+        return -4;
+    *cus = p.multiProcessorCount;
+    return 0;
+}
+
+template <int MODE>
+hipError_t launch_mode(int w, unsigned blocks, int iters, uint64_t* out, hipStream_t s)
+{
+    switch (w) {
+    case 2: hipLaunchKernelGGL((step_kernel<MODE, 2>), dim3(blocks), dim3(256), 0, s, iters, out); break;
+    case 3: hipLaunchKernelGGL((step_kernel<MODE, 3>), dim3(blocks), dim3(256), 0, s, iters, out); break;
+    default: hipLaunchKernelGGL((step_kernel<MODE, 4>), dim3(blocks), dim3(256), 0, s, iters, out); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int64_t qpg_calib_step_blocks(int waves_per_simd)
+{
+    int cus = 0;
+    if (waves_per_simd < 2 || waves_per_simd > 4 || check_device(&cus) != 0) return 0;
+    return (int64_t)cus * waves_per_simd;
+}
+
+extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream)
+{
+    if (!out || mode < 0 || mode > 3 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
+        return -1;
+    if (((uintptr_t)out & 7) != 0) return -2;
+    int cus = 0;
+    const int dv = check_device(&cus);
+    if (dv != 0) return dv;
+    const unsigned blocks = (unsigned)(cus * waves_per_simd);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (mode) {
+    case 0: e = launch_mode<0>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 1: e = launch_mode<1>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 2: e = launch_mode<2>(waves_per_simd, blocks, (int)iters, out, s); break;
+    default: e = launch_mode<3>(waves_per_simd, blocks, (int)iters, out, s); break;
+    }
+    return e == hipSuccess ? 0 : -3;
+}

@@ -107,17 +107,19 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // Written as inline asm so that the compiler does not track it: its own wait insertion
 // can make unrelated LDS reads of the stage being computed wait for the prefetch.
 // Completion is waited for explicitly (wait_vmem) before the barrier that publishes the
-// stage. The LDS base must be wave-uniform.
+// stage. The LDS base must be wave-uniform: it is the m0 operand of the instruction, bound
+// to that register by the "{m0}" constraint, so the compiler writes m0 itself and knows
+// that the statement reads it.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(la) : "memory");
 }
 
 // KS = number of four-wave groups per workgroup; group g computes the tile over its own
 // contiguous range of super-blocks and the partial sums are added in group order at the end.
 template <bool ISUMS, int KS>
-__global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
+__global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qplane,
                                                          const uint32_t* __restrict__ hdr,
                                                          float* __restrict__ Y,

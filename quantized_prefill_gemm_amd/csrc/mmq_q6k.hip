@@ -91,17 +91,19 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // One dword LDS-direct load: each lane's 4 bytes at voff go to LDS byte lds_wave_base + 4*lane.
 // Inline asm, so that the compiler's own waits do not tie unrelated LDS reads to it;
 // completion is waited for explicitly (wait_vmem) before the barrier that publishes it.
+// The wave-uniform LDS base is the instruction's m0 operand ("{m0}" constraint: the
+// compiler writes m0 itself and knows that the statement reads it).
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(la) : "memory");
 }
 
 // 16-byte form of the same load: lane L's 16 bytes at voff go to LDS byte lds_wave_base + 16L.
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(la) : "memory");
 }
 
 // Prepared q6_K weights: per 128-row tile T and super-block sb, two 16 KiB stage images
@@ -118,7 +120,7 @@ static_assert(offsetof(StageLds, bh) == offsetof(StageLds, bl) + TN * 64 &&
 // PREP: W is the prepared layout (16-byte aligned, no register staging, the q8 tile in
 // natural order by 16-byte loads and its operands read as two 8-byte halves).
 template <bool ISUMS, int KS, bool PREP>
-__global__ void __launch_bounds__(256 * KS, (ISUMS || KS > 1) ? 1 : 3) mmq_q6K_kernel(
+__global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
     float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total, int pieces)
 {

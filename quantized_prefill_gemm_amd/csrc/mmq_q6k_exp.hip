@@ -100,23 +100,25 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // LDS-direct loads (inline asm, so that the compiler's own waits do not tie unrelated LDS
 // reads to them; completion is waited for explicitly before the barrier that publishes
-// them): lane L's 4 / 16 bytes at voff go to LDS byte lds_wave_base + 4L / 16L.
+// them): lane L's 4 / 16 bytes at voff go to LDS byte lds_wave_base + 4L / 16L. The
+// wave-uniform LDS base is the instruction's m0 operand ("{m0}" constraint: the compiler
+// writes m0 itself and knows that the statement reads it).
 __device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+    asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(la) : "memory");
 }
 __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, int voff)
 {
     const unsigned la = (unsigned)(uintptr_t)(lds_void*)lds_wave_base;
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "s"(la) : "memory", "m0");
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r), "{m0}"(la) : "memory");
 }
 
 // KS groups of 4 waves over contiguous super-block ranges (few tiles), or KW = 2: 8 waves
 // on one tile, waves w and w + 4 computing the same sub-tile over chunks 0-1 and 2-3 of each
 // stage (four waves per SIMD with two workgroups per CU).
 template <bool CSUMS, int KS, int KW>
-__global__ void __launch_bounds__(256 * KS * KW, (CSUMS || KS > 1) ? 1 : (KW > 1 ? 2 : 3)) mmq_q6K_exp_kernel(
+__global__ void __launch_bounds__(256 * KS * KW, KS > 1 ? 1 : (KW > 1 ? 2 : 3)) mmq_q6K_exp_kernel(
     const uint8_t* __restrict__ WE, const int8_t* __restrict__ qplane, const uint32_t* __restrict__ hdr,
     float* __restrict__ Y, int32_t* __restrict__ S, int M, int N, int K, int tiles_m, int total, int pieces)
 {

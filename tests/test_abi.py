@@ -219,9 +219,30 @@ def test_calib_library_exports_and_rejects():
     if not os.path.exists(CALIB):
         pytest.skip("libqpg_calib.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
-    names = re.findall(r"^\s*int\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
-    assert names == ["qpg_calib_mfma_i8"]
+    names = re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    assert names == ["qpg_calib_mfma_i8", "qpg_calib_step", "qpg_calib_step_blocks", "qpg_probe_mfma"]
     lib = ctypes.CDLL(CALIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    st = lib.qpg_calib_step
+    st.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    st.restype = ctypes.c_int
+    assert st(4, 3, 100, A16, None) == EINVAL           # mode
+    assert st(2, 1, 100, A16, None) == EINVAL           # waves per SIMD
+    assert st(2, 5, 100, A16, None) == EINVAL
+    assert st(2, 3, 0, A16, None) == EINVAL             # iters
+    assert st(2, 3, 100, None, None) == EINVAL
+    assert st(2, 3, 100, ctypes.c_void_p((1 << 20) + 4), None) == EALIGN
+    pr = lib.qpg_probe_mfma
+    pr.argtypes = [ctypes.c_int] + [ctypes.c_void_p] * 5
+    pr.restype = ctypes.c_int
+    assert pr(3, A16, A16, A16, A16, None) == EINVAL
+    assert pr(0, None, A16, A16, A16, None) == EINVAL
+    assert pr(0, A8, A16, A16, A16, None) == EALIGN
+    assert pr(2, A16, A16, A8, A16, None) == EALIGN
+    if not _has_gpu():
+        assert st(2, 3, 100, A16, None) == EDEVICE
+        assert pr(1, A8, A8, A16, A16, None) == EDEVICE     # 8-byte operands suffice for kind 1
     f = lib.qpg_calib_mfma_i8
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
@@ -233,3 +254,93 @@ def test_calib_library_exports_and_rejects():
     assert f(512, 100, ctypes.c_void_p((1 << 20) + 4), None) == EALIGN
     if not _has_gpu():
         assert f(512, 100, A16, None) == EDEVICE
+
+
+# ---------------------------------------------------------------------------- binding checks
+# The binding must refuse caller-supplied outputs that are too small (the C ABI takes no
+# output size). Host-only: the is-a-device-tensor check and the stream lookup are bypassed,
+# the size helpers come from the real library, and the compute entry points are replaced by
+# a recorder, so a call that passes validation is seen without any kernel being launched.
+
+@pytest.fixture
+def recorded(monkeypatch, L):
+    from quantized_prefill_gemm_amd import binding as Bd
+    calls = []
+
+    real = Bd.lib()
+
+    class Recorder:
+        def __getattr__(self, name):
+            if name.startswith("qpg_"):
+                return getattr(real, name)
+            def f(*a):
+                calls.append(name)
+                return 0
+            return f
+
+    monkeypatch.setattr(Bd, "lib", lambda: Recorder())
+
+    def dev_host(t, dtype, name):
+        if t.dtype != dtype:
+            raise Bd.QPGError(Bd.QPG_EINVAL, f"{name} dtype")
+        if not t.is_contiguous():
+            raise Bd.QPGError(Bd.QPG_EINVAL, f"{name} contiguity")
+
+    monkeypatch.setattr(Bd, "_dev", dev_host)
+    monkeypatch.setattr(Bd, "_stream", lambda stream=None: None)
+    return Bd, calls
+
+
+def test_binding_rejects_undersized_outputs(recorded):
+    import torch
+    Bd, calls = recorded
+    M, N, K = 64, 200, 512
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)
+    w4, w6 = u8(N * 2 * 144), u8(N * 2 * 210)
+    xq, x = u8(Bd.q8_1_bytes(M, K)), f32(M, K)
+    wp, we = u8(Bd.q6K_prep_bytes(N, K)), u8(Bd.q6K_exp_bytes(N, K))
+    cases = [   # (call with a full-size output, call with an output one element short, entry reached)
+        (lambda o: Bd.mmq_q4K_q8(w4, xq, M, N, K, o), f32(M * N), "mmq_q4K_q8"),
+        (lambda o: Bd.mmq_q6K_q8(w6, xq, M, N, K, o), f32(M * N), "mmq_q6K_q8"),
+        (lambda o: Bd.mmq_q4K_isums(w4, xq, M, N, K, o), i32(M * N * K // 32), "mmq_q4K_isums"),
+        (lambda o: Bd.mmq_q6K_isums(w6, xq, M, N, K, o), i32(M * N * K // 16), "mmq_q6K_isums"),
+        (lambda o: Bd.mmq_q6K_prep_q8(wp, xq, M, N, K, o), f32(M * N), "mmq_q6K_prep_q8"),
+        (lambda o: Bd.mmq_q6K_prep_isums(wp, xq, M, N, K, o), i32(M * N * K // 16), "mmq_q6K_prep_isums"),
+        (lambda o: Bd.mmq_q6K_exp_q8(we, xq, M, N, K, o), f32(M * N), "mmq_q6K_exp_q8"),
+        (lambda o: Bd.mmq_q6K_exp_csums(we, xq, M, N, K, o), i32(M * N * K // 32), "mmq_q6K_exp_csums"),
+        (lambda o: Bd.mmq_q4K(w4, x, N, y=o), f32(M * N), "mmq_q4K"),
+        (lambda o: Bd.mmq_q4K(w4, x, N, xq_ws=o), u8(Bd.q8_1_bytes(M, K)), "mmq_q4K"),
+        (lambda o: Bd.mmq_q6K(w6, x, N, y=o), f32(M * N), "mmq_q6K"),
+        (lambda o: Bd.quantize_q8_1(x, o), u8(Bd.q8_1_bytes(M, K)), "quantize_q8_1"),
+        (lambda o: Bd.q6K_prepare(w6, N, K, wp=o), u8(Bd.q6K_prep_bytes(N, K)), "q6K_prepare"),
+        (lambda o: Bd.q6K_expand(w6, N, K, we=o), u8(Bd.q6K_exp_bytes(N, K)), "q6K_expand"),
+        (lambda o: Bd.mmq_q4K_q8_sk(w4, xq, M, N, K, y=o), f32(M * N), "mmq_q4K_q8_sk"),
+        (lambda o: Bd.mmq_q6K_exp_q8_sk(we, xq, M, N, K, y=o), f32(M * N), "mmq_q6K_exp_q8_sk"),
+    ]
+    for call, full, entry in cases:
+        calls.clear()
+        call(full)
+        assert calls == [entry], (entry, calls)
+        calls.clear()
+        with pytest.raises(Bd.QPGError) as e:
+            call(full[:-1])
+        assert e.value.status == Bd.QPG_EINVAL, entry
+        assert calls == [], f"{entry} reached the library with an undersized output"
+
+
+def test_binding_rejects_undersized_splitk_workspace(recorded):
+    import torch
+    Bd, calls = recorded
+    M, N, K = 64, 100, 1536                    # one tile, six super-blocks: two pieces
+    nws = Bd.mmq_sk_bytes(M, N, K, "q4K")
+    assert nws == 2 * M * N * 4
+    w = torch.zeros(N * 6 * 144, dtype=torch.uint8)
+    xq = torch.zeros(Bd.q8_1_bytes(M, K), dtype=torch.uint8)
+    Bd.mmq_q4K_q8_sk(w, xq, M, N, K, ws=torch.zeros(nws // 4, dtype=torch.float32))
+    assert calls == ["mmq_q4K_q8_sk"]
+    calls.clear()
+    with pytest.raises(Bd.QPGError):
+        Bd.mmq_q4K_q8_sk(w, xq, M, N, K, ws=torch.zeros(nws // 4 - 1, dtype=torch.float32))
+    assert calls == []
