@@ -14,7 +14,9 @@
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers of the current HIP device. The caller owns every
  *     buffer; the library allocates and frees nothing, prints nothing and keeps no
- *     state besides a per-device cache of device properties.
+ *     state besides per-device caches (device properties; the address of the fixed
+ *     scratch of mmq_q4K_noalloc, a device array the runtime places on each device when
+ *     the library's code loads there).
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream); nothing
  *     synchronises. Buffers must stay valid until the stream reaches the work.
  *   - Shapes: M = tokens, N = output features (weight rows), K = input features.
@@ -24,7 +26,8 @@
  *     QPG_EALIGN and QPG_EDEVICE nothing has been. QPG_EHIP reports a failed kernel
  *     launch; in the entry points that enqueue two kernels (mmq_q4K / mmq_q6K: quantise,
  *     then the MMQ; the _sk entry points with a split: the MMQ, then the reduce) the first
- *     may already be enqueued when the second fails. There is no fallback path.
+ *     may already be enqueued when the second fails. QPG_ESCRATCH (mmq_q4K_noalloc only)
+ *     is reported before anything is enqueued. There is no fallback path.
  *   - The library runs on gfx950 only (QPG_EDEVICE otherwise).
  *
  * Data layouts
@@ -66,7 +69,8 @@ enum {
     QPG_EINVAL = -1,   /* null pointer, bad shape (M/N < 1, K % 256, too large)   */
     QPG_EALIGN = -2,   /* a pointer violates its alignment requirement           */
     QPG_EHIP = -3,     /* the HIP runtime reported an error when enqueuing        */
-    QPG_EDEVICE = -4   /* current device is not gfx950 or cannot be queried       */
+    QPG_EDEVICE = -4,  /* current device is not gfx950 or cannot be queried       */
+    QPG_ESCRATCH = -5  /* more than the fixed scratch of mmq_q4K_noalloc needed   */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -103,6 +107,24 @@ int mmq_q4K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64
             void* xq_ws, qpg_stream_t stream);
 int mmq_q6K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
             void* xq_ws, qpg_stream_t stream);
+
+/*
+ * mmq_q4K_noalloc: mmq_q4K without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The q8_1 activations go to a fixed device array of
+ * QPG_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every device it runs on
+ * until the process ends; the call itself allocates nothing. Shapes whose q8_1 buffer,
+ * qpg_q8_1_bytes(M, K), exceeds the array are refused with QPG_ESCRATCH before anything
+ * is enqueued (e.g. M * K <= 29.8 M values: 2048 x 11008 or 4096 x 4096 fit). Same result
+ * as mmq_q4K, bit for bit. The first call on a device looks up the array's device address
+ * (a host-side runtime query, no stream work); make it outside graph capture. All calls
+ * on one device share its array and the last call's q8_1 data stays in it: calls that
+ * overlap in time on one device (two streams, two threads) race and must be serialised
+ * by the caller. Alignment: w, x 16 bytes; y 4 bytes.
+ */
+#define QPG_NOALLOC_SCRATCH_BYTES (32u << 20)
+int mmq_q4K_noalloc(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K,
+                    qpg_stream_t stream);
 
 /* The MMQ kernels alone, on an already quantised q8_1 buffer xq. */
 int mmq_q4K_q8(const void* w, const void* xq, float* y, int64_t M, int64_t N, int64_t K,

@@ -14,7 +14,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqpg.so")
 
-QPG_OK, QPG_EINVAL, QPG_EALIGN, QPG_EHIP, QPG_EDEVICE = 0, -1, -2, -3, -4
+QPG_OK, QPG_EINVAL, QPG_EALIGN, QPG_EHIP, QPG_EDEVICE, QPG_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20     # QPG_NOALLOC_SCRATCH_BYTES of qpg.h
 
 
 class QPGError(RuntimeError):
@@ -41,6 +42,8 @@ def lib() -> ctypes.CDLL:
         L.quantize_q8_1.argtypes = [P, P, I64, I64, P]
         for f in (L.mmq_q4K, L.mmq_q6K):
             f.argtypes = [P, P, P, I64, I64, I64, P, P]
+        L.mmq_q4K_noalloc.argtypes = [P, P, P, I64, I64, I64, P]
+        L.mmq_q4K_noalloc.restype = ctypes.c_int
         for f in (L.mmq_q4K_q8, L.mmq_q6K_q8, L.mmq_q4K_isums, L.mmq_q6K_isums):
             f.argtypes = [P, P, P, I64, I64, I64, P]
         L.qpg_q6K_prep_bytes.argtypes = [I64, I64]
@@ -70,7 +73,7 @@ EXPORTS = ("qpg_strerror", "qpg_q8_1_bytes", "quantize_q8_1", "mmq_q4K", "mmq_q6
            "mmq_q6K_q8", "mmq_q4K_isums", "mmq_q6K_isums", "qpg_q6K_prep_bytes", "q6K_prepare",
            "mmq_q6K_prep_q8", "mmq_q6K_prep_isums", "qpg_q6K_exp_bytes", "q6K_expand", "mmq_q6K_exp_q8",
            "mmq_q6K_exp_csums", "qpg_mmq_sk_bytes", "mmq_q4K_q8_sk", "mmq_q6K_q8_sk", "mmq_q6K_prep_q8_sk",
-           "mmq_q6K_exp_q8_sk")
+           "mmq_q6K_exp_q8_sk", "mmq_q4K_noalloc")
 
 
 def _check(rc: int, what: str):
@@ -156,6 +159,18 @@ def mmq_q4K(w: torch.Tensor, x: torch.Tensor, N: int, y=None, xq_ws=None, stream
 
 def mmq_q6K(w: torch.Tensor, x: torch.Tensor, N: int, y=None, xq_ws=None, stream=None) -> torch.Tensor:
     return _mmq("q6K", w, x, N, y, xq_ws, stream)
+
+
+def mmq_q4K_noalloc(w: torch.Tensor, x: torch.Tensor, N: int, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """mmq_q4K with the q8_1 activations in the library's fixed per-device scratch: the C call
+    allocates nothing (y is the caller's). Calls overlapping on one device race."""
+    _dev(x, torch.float32, "x")
+    M, K = x.shape
+    _wcheck(w, N, K, 144)
+    _same_device(w, x, "w")
+    _out(y, torch.float32, "y", M * N, x)
+    _check(lib().mmq_q4K_noalloc(_ptr(w), _ptr(x), _ptr(y), M, N, K, _stream(stream)), "mmq_q4K_noalloc")
+    return y
 
 
 def _mmq_q8(which: str, w, xq, M, N, K, out, stream, isums: bool):

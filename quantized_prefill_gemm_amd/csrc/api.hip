@@ -45,6 +45,31 @@ int check_mmq_shape(int64_t M, int64_t N, int64_t K)
     return QPG_OK;
 }
 
+// ---- The allocation-free entry point's scratch: one fixed array per device, holding the q8_1
+// activations that mmq_q4K otherwise writes into the caller's workspace. The runtime
+// places a copy on every device the library runs on when the code object loads there; it
+// lives until the process ends. Host code never passes the array's name to a kernel (on
+// the host it names a stand-in, not device memory): the device address of each copy is
+// looked up once per device with hipGetSymbolAddress, that device being current, and
+// cached.
+static __device__ __align__(256) uint8_t scratch[QPG_NOALLOC_SCRATCH_BYTES];
+void* g_scratch[64];
+std::mutex g_scratch_mu;
+
+int scratch_of_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QPG_EDEVICE;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QPG_EHIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return QPG_OK;
+}
+
 int status_of(hipError_t e)
 {
     if (e == hipSuccess) return QPG_OK;
@@ -282,6 +307,7 @@ const char* qpg_strerror(int status)
     case QPG_EALIGN: return "pointer alignment requirement violated";
     case QPG_EHIP: return "HIP runtime error while enqueuing";
     case QPG_EDEVICE: return "current device is not gfx950 (MI355X) or cannot be queried";
+    case QPG_ESCRATCH: return "q8_1 activations larger than the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
     }
 }
@@ -346,6 +372,24 @@ int mmq_q6K(const void* w, const float* x, float* y, int64_t M, int64_t N, int64
             qpg_stream_t stream)
 {
     return mmq_f32(true, w, x, y, M, N, K, xq_ws, stream);
+}
+
+int mmq_q4K_noalloc(const void* w, const float* x, float* y, int64_t M, int64_t N, int64_t K, qpg_stream_t stream)
+{
+    if (!w || !x || !y) return QPG_EINVAL;
+    int rc = check_mmq_shape(M, N, K);
+    if (rc != QPG_OK) return rc;
+    if (qpg_q8_1_bytes(M, K) > (size_t)QPG_NOALLOC_SCRATCH_BYTES) return QPG_ESCRATCH;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 4)) return QPG_EALIGN;
+    rc = check_device();
+    if (rc != QPG_OK) return rc;
+    void* xq = nullptr;
+    rc = scratch_of_current_device(&xq);
+    if (rc != QPG_OK) return rc;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    rc = quantize_checked(x, xq, M, K, s);
+    if (rc != QPG_OK) return rc;
+    return mmq_checked(false, w, xq, y, nullptr, M, N, K, s);
 }
 
 }  // extern "C"

@@ -50,6 +50,8 @@ def L():
     lib.qpg_mmq_sk_bytes.argtypes = [I64, I64, I64, ctypes.c_int]
     for f in (lib.mmq_q4K_q8_sk, lib.mmq_q6K_q8_sk, lib.mmq_q6K_prep_q8_sk, lib.mmq_q6K_exp_q8_sk):
         f.argtypes = [P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.mmq_q4K_noalloc.argtypes = [P, P, P, I64, I64, I64, P]
+    lib.mmq_q4K_noalloc.restype = ctypes.c_int
     return lib
 
 
@@ -344,3 +346,26 @@ def test_binding_rejects_undersized_splitk_workspace(recorded):
     with pytest.raises(Bd.QPGError):
         Bd.mmq_q4K_q8_sk(w, xq, M, N, K, ws=torch.zeros(nws // 4 - 1, dtype=torch.float32))
     assert calls == []
+
+
+ESCRATCH = -5
+NOALLOC_SCRATCH = 32 << 20
+
+
+def test_noalloc_entry_rejects_before_enqueue(L):
+    f = L.mmq_q4K_noalloc
+    assert L.qpg_strerror(ESCRATCH)
+    assert "#define QPG_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
+    K = 11008 - 11008 % 256 + 256                       # 11264: a multiple of 256
+    fits = NOALLOC_SCRATCH // L.qpg_q8_1_bytes(1, K)
+    assert L.qpg_q8_1_bytes(fits, K) <= NOALLOC_SCRATCH < L.qpg_q8_1_bytes(fits + 1, K)
+    assert f(A16, A16, A16, fits + 1, 256, K, None) == ESCRATCH     # one token row too many
+    assert f(None, A16, A16, 64, 256, 256, None) == EINVAL
+    assert f(A16, None, A16, 64, 256, 256, None) == EINVAL
+    assert f(A16, A16, None, 64, 256, 256, None) == EINVAL
+    assert f(A16, A16, A16, 64, 256, 288, None) == EINVAL
+    assert f(A8, A16, A16, 64, 256, 256, None) == EALIGN              # q4_K weights: 16 bytes
+    assert f(A16, A8, A16, 64, 256, 256, None) == EALIGN              # x: 16 bytes
+    assert f(A16, A16, A2, 64, 256, 256, None) == EALIGN              # y: 4 bytes
+    if not _has_gpu():
+        assert f(A16, A16, A16, fits, 256, K, None) == EDEVICE       # the largest shape passes validation
