@@ -56,6 +56,15 @@ int64_t qpg_calib_step_blocks(int waves_per_simd);
  * -3 (launch error) or -4 (not gfx950). */
 int qpg_probe_mfma(int kind, const void* a, const void* b, const void* c, void* d, void* stream);
 
+/* LDS-direct load probe: one wave issues one buffer_load_dword (width 4) or
+ * buffer_load_dwordx4 (width 16) with the LDS flag, lane l reading at byte offset voff[l] of
+ * the nbytes-byte buffer src (a buffer descriptor of that range: offsets past it read zeros),
+ * into a 1 KiB LDS array pre-filled with 0xDEADBEEF, which is then copied to out (256
+ * uint32). Device pointers owned by the caller: src 16-byte aligned, voff (64 int32) and out
+ * 4-byte aligned. Asynchronous on `stream`. Returns 0, -1 (null pointer, width not 4 or 16,
+ * nbytes outside [1, 2^30]), -2 (alignment), -3 (launch error) or -4 (not gfx950). */
+int qpg_probe_lds_dma(int width, const void* src, int64_t nbytes, const int32_t* voff, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -71,3 +71,51 @@ extern "C" int qpg_probe_mfma(int kind, const void* a, const void* b, const void
     }
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// ---- LDS-direct load probe: one wave issues one buffer_load_dword / _dwordx4 with the LDS
+// flag from host-chosen per-lane source offsets into a buffer of nbytes bytes; the LDS
+// contents (pre-filled with 0xDEADBEEF) are then copied out. Shows where lane L's bytes land
+// (4 L / 16 L), that any per-lane source offset is honoured (permutations, offsets that are
+// not multiples of the load size), and that offsets past the buffer read as zeros.
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int WIDTH>
+__global__ void __launch_bounds__(64) probe_lds_dma_kernel(const uint8_t* src, int nbytes, const int* voff, uint32_t* out)
+{
+    __shared__ uint32_t buf[256];
+    const int l = (int)threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf[4 * l + i] = 0xDEADBEEFu;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, nbytes, 0x00020000);
+    const unsigned la = (unsigned)(uintptr_t)(lds_void*)buf;
+    const int v = voff[l];
+    if constexpr (WIDTH == 16)
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(v), "s"(r), "{m0}"(la) : "memory");
+    else
+        asm volatile("buffer_load_dword %0, %1, 0 offen lds" : : "v"(v), "s"(r), "{m0}"(la) : "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the load has written LDS
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[4 * l + i] = buf[4 * l + i];
+}
+
+}  // namespace
+
+extern "C" int qpg_probe_lds_dma(int width, const void* src, int64_t nbytes, const int32_t* voff, uint32_t* out,
+                                 void* stream)
+{
+    if (!src || !voff || !out || (width != 4 && width != 16) || nbytes < 1 || nbytes > (1 << 30)) return -1;
+    if (((uintptr_t)src & 15) || ((uintptr_t)voff & 3) || ((uintptr_t)out & 3)) return -2;
+    if (!is_gfx950()) return -4;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (width == 16)
+        hipLaunchKernelGGL(probe_lds_dma_kernel<16>, dim3(1), dim3(64), 0, s, static_cast<const uint8_t*>(src),
+                           (int)nbytes, voff, out);
+    else
+        hipLaunchKernelGGL(probe_lds_dma_kernel<4>, dim3(1), dim3(64), 0, s, static_cast<const uint8_t*>(src),
+                           (int)nbytes, voff, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}

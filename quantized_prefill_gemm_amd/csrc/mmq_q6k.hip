@@ -17,17 +17,22 @@
 //  * The MFMA accumulates onto the bits of 1.5*2^23, so its int32 result read as f32 is
 //    1.5*2^23 + J exactly (|J| <= 32*127*16 < 2^22): e = fma(F, da, -1.5*2^23*da) is
 //    round(da*J) and y = fma(e, d*sc, y). Two VALU ops per output and sub-block.
-//  * Staging is a two-deep pipeline of half super-blocks (128 k, one barrier per stage).
-//    The q8 tile of stage h+1 comes by 16-byte LDS-direct loads (buffer_load_dwordx4 ...
-//    lds) in natural order, issued before stage h is computed, and the q8_1 header words
-//    of the stage by dword LDS-direct loads. The weight bytes of stage h+1 (rows start only
-//    2-byte aligned: 210-byte blocks) are fetched into registers as aligned dwords at the
-//    same time, shifted into place with v_alignbyte and written to the other LDS buffer
-//    after stage h's compute, together with d*sc.
+//  * Staging is a two-deep pipeline of half super-blocks (128 k, one barrier per stage),
+//    all of it by LDS-direct loads issued one stage ahead: the q8 tile by 16-byte loads
+//    (buffer_load_dwordx4 ... lds) in natural order, the q8_1 header words by dword loads,
+//    and the raw weight bytes by dword loads straight into the stage layout below. A lane's
+//    source offset may be any byte offset (rows of 210-byte blocks start only 2-byte
+//    aligned when K/256 is odd), so the per-lane offsets apply the layout's piece swap and
+//    row swizzle during the copy, with no register staging and no shifts. Each wave loads
+//    exactly its own 32 weight rows (and their int8 scales and d), so after its own load
+//    wait it converts their d*sc for the stage without another barrier; the barrier is for
+//    the q8 tile and header words, which every wave reads.
 //  * LDS: inside every 32-byte group of ql and qh the 8-byte pieces 1 and 2 are swapped, so
 //    one 16-byte read gives a lane its 8 bytes of both sub-blocks of a chunk (k-group l>>5
 //    of each K=16 MFMA); the matching q8 operand is two 8-byte reads. Rows are XOR-swizzled
-//    in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups.
+//    in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups. The prepared
+//    weight form (q6K_prepare) is this stage layout written once to memory, with d*sc
+//    included, staged by plain 16-byte copies.
 //  * When the matrix has at most one tile per CU, three groups of four waves share a
 //    workgroup, each over a contiguous range of super-blocks, and the partial tiles are
 //    added in group order through LDS at the end (three waves per SIMD, deterministic).
@@ -56,12 +61,16 @@ struct StageLds {
     alignas(16) uint8_t bh[TN * 32];
     alignas(16) float dsc[8][TN];       // d*sc per sub-block of the stage, rows in C-register order per wave
     alignas(16) uint32_t hw[4][TM];     // q8_1 header words (fp16 da | ssum) per chunk of the stage and token
-    alignas(16) uint32_t spare[256];    // keeps a group at 52 KiB (three per CU)
+    // raw blocks: each wave's 32 rows, the stage's 8 int8 scales (2 words per row) and the word
+    // holding fp16 d (block bytes 206..209: d in the high half), as loaded
+    alignas(16) uint32_t wsc[4][64];
+    alignas(16) uint32_t wd[4][32];
 };
 struct GroupLds {
     StageLds st[2];
 };
-static_assert(sizeof(GroupLds) == 53248, "LDS of one group");
+static_assert(sizeof(GroupLds) == 54272, "LDS of one group");
+static_assert(3 * sizeof(GroupLds) <= 160 * 1024, "three groups per CU");
 static_assert(sizeof(GroupLds) >= TM * TN * 4, "a group's buffers hold its partial tile");
 
 __device__ __forceinline__ int aq_sw(int t) { return (t >> 1) & 7; }
@@ -162,45 +171,62 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
         const int t = 8 * (2 * wave + i) + (lane >> 3);
         voQ16[i] = t * K + 16 * ((lane & 7) ^ aq_sw(t));
     }
-    auto issue_q8 = [&](int sb, int hh, StageLds& st) {
+    // Raw blocks: the stage's bytes go straight into the prepared stage layout by dword
+    // LDS-direct loads whose per-lane source offsets apply the piece swap and the row swizzle
+    // (a lane may read at any byte offset: rows of 210-byte blocks start 2-byte aligned).
+    // LDS dword s of bl is dword dw = s & 3 of slot G = (s >> 2) & 3 of row j = s >> 4; the
+    // slot holds logical granule G ^ bl_sw(j) = 2 g + x, i.e. the ql dwords 8g + 2x, 8g + 2x + 1,
+    // 8g + 4 + 2x, 8g + 5 + 2x of the row's stage half. bh likewise with 8 dwords per row
+    // (qh dwords 2x, 2x + 1, 4 + 2x, 5 + 2x in slot x ^ bh_sw(j)). Slab i = 64 dwords; wave w
+    // loads ql slabs 8w..8w+7 and qh slabs 4w..4w+3, i.e. exactly its own 32 rows, and the
+    // scales and d of those rows.
+    unsigned voL[8], voB[4], voS = 0, voD = 0;
+    if constexpr (!PREP) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int sl = 64 * (8 * wave + i) + lane;
+            const int j = sl >> 4, dw = sl & 3, gp = ((sl >> 2) & 3) ^ bl_sw(j);
+            voL[i] = (unsigned)(j * wrow + 4 * (8 * (gp >> 1) + 2 * (gp & 1) + (dw & 1) + 4 * (dw >> 1)));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = 64 * (4 * wave + i) + lane;
+            const int j = sl >> 3, dw = sl & 3, x = ((sl >> 2) & 1) ^ bh_sw(j);
+            voB[i] = (unsigned)(j * wrow + 4 * (2 * x + (dw & 1) + 4 * (dw >> 1)));
+        }
+        voS = (unsigned)((32 * wave + (lane >> 1)) * wrow + 4 * (lane & 1));
+        voD = (unsigned)((32 * wave + (lane & 31)) * wrow);
+    }
+    const uint8_t* const wbase = W + (size_t)n0 * wrow;
+    const unsigned nW = (unsigned)(rows_w * wrow);
+    // A descriptor over this tile's rows starting at byte `off` of every row's first block
+    // (the stage offset moves the base and shrinks the range by the same amount, so loads
+    // of rows past N still fall outside it and read zeros).
+    auto wdesc = [&](unsigned off) {
+        off = __builtin_amdgcn_readfirstlane(off);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(wbase + off), 0, (int)(nW - off), 0x00020000);
+    };
+    auto issue_stage = [&](int sb, int hh, StageLds& st) {
         const int off = sb * QK_K + hh * HALF;
 #pragma unroll
         for (int i = 0; i < 2; ++i) lds_load16(rQ, st.aq + 1024 * (2 * wave + i), voQ16[i] + off);
-        if constexpr (PREP)
+        if constexpr (PREP) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 lds_load16(rW, st.bl + 1024 * (4 * wave + i), (sb * 2 + hh) * PREP_STAGE + 1024 * (4 * wave + i) + 16 * lane);
-        if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
-    };
-
-    // ---- weights of one stage into registers. Task A (all threads): ql group tid >> 7
-    // (32 bytes) of row tid & 127; task B (threads < 128): the qh half (32 bytes) of row
-    // tid, sc[8hh..8hh+7] and d. Each 32-byte group is 9 aligned dwords from
-    // (block + offset - sh), sh = block offset & 2.
-    struct Pre {
-        uint32_t a[9], b[9], sc[3], dh;
-    };
-    auto load_stage = [&](int sb, int hh, Pre& p) {
-        const int jA = tid & 127, grpA = tid >> 7;
-        const int oA = jA * wrow + sb * Q6K_BYTES;
-        const int shA = oA & 2;
-        const int srcA = oA + 64 * hh + 32 * grpA - shA;
+        } else {
+            const unsigned blk = (unsigned)(sb * Q6K_BYTES);
+            const __amdgpu_buffer_rsrc_t rL = wdesc(blk + 64 * hh), rB = wdesc(blk + 128 + 32 * hh);
 #pragma unroll
-        for (int i = 0; i < 9; ++i) p.a[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcA + 4 * i, 0, 0);
-        if (tid < TN) {
-            const int srcB = oA + 128 + 32 * hh - shA;
+            for (int i = 0; i < 8; ++i) lds_load4(rL, st.bl + 256 * (8 * wave + i), (int)voL[i]);
 #pragma unroll
-            for (int i = 0; i < 9; ++i) p.b[i] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcB + 4 * i, 0, 0);
+            for (int i = 0; i < 4; ++i) lds_load4(rB, st.bh + 256 * (4 * wave + i), (int)voB[i]);
             if constexpr (!ISUMS) {
-                // sc[8hh..8hh+7] at oA + 192 + 8hh: 2 aligned dwords, a third when shifted (the
-                // third never passes the block end: it ends at oA + 202 + 8hh)
-                const int srcS = oA + 192 + 8 * hh - shA;
-                p.sc[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS, 0, 0);
-                p.sc[1] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS + 4, 0, 0);
-                p.sc[2] = shA ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rW, srcS + 8, 0, 0) : 0u;
-                p.dh = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rW, oA + 208, 0, 0);
+                lds_load4(wdesc(blk + 192 + 8 * hh), &st.wsc[wave][0], (int)voS);
+                if (lane < 32) lds_load4(wdesc(blk + 206), &st.wd[wave][0], (int)voD);
             }
         }
+        if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
     };
     int32x16 magic;
 #pragma unroll
@@ -214,40 +240,16 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
     const int wr = 32 * wave + l32;                  // weight row of this lane's A operand
     const int tsw = aq_sw(l32);                      // tokens l32 and l32 + 32 share the swizzle
 
-    // Write a stage's prefetched weight bytes and d*sc into LDS.
-    auto commit = [&](const Pre& p, int sb, StageLds& st) {
-        const int jA = tid & 127, grpA = tid >> 7;
-        const int shA = (jA * wrow + sb * Q6K_BYTES) & 2;
-        uint32_t ga[8];
+    // d*sc of this wave's 32 rows for the stage's 8 sub-blocks, from the scale words and d the
+    // wave loaded itself (so only its own load wait is needed): lane (jj, half) converts the
+    // four scales 4 half .. 4 half + 3 of row 32 wave + jj.
+    auto decode_dsc = [&](StageLds& st) {
+        const int jj = l32;
+        const uint32_t scw = st.wsc[wave][2 * jj + hg];
+        const float d = half_bits_to_float(st.wd[wave][jj] >> 16);
+        const int pos = 32 * wave + c_pos(jj);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ga[i] = __builtin_amdgcn_alignbyte(p.a[i + 1], p.a[i], shA);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int Gl = 2 * grpA + x;
-            const uint32x4 v = {ga[2 * x], ga[2 * x + 1], ga[4 + 2 * x], ga[5 + 2 * x]};
-            *reinterpret_cast<uint32x4*>(st.bl + 64 * jA + 16 * (Gl ^ bl_sw(jA))) = v;
-        }
-        if (tid < TN) {
-            uint32_t gb[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) gb[i] = __builtin_amdgcn_alignbyte(p.b[i + 1], p.b[i], shA);
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const uint32x4 v = {gb[2 * x], gb[2 * x + 1], gb[4 + 2 * x], gb[5 + 2 * x]};
-                *reinterpret_cast<uint32x4*>(st.bh + 32 * jA + 16 * (x ^ bh_sw(jA))) = v;
-            }
-            if constexpr (!ISUMS) {
-                const uint32_t s0 = __builtin_amdgcn_alignbyte(p.sc[1], p.sc[0], shA);
-                const uint32_t s1 = __builtin_amdgcn_alignbyte(p.sc[2], p.sc[1], shA);
-                const float d = half_bits_to_float(p.dh & 0xFFFFu);
-                const int pos = 32 * (jA >> 5) + c_pos(jA & 31);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const uint32_t w = u < 4 ? s0 : s1;
-                    st.dsc[u][pos] = d * (float)(int)(int8_t)(w >> (8 * (u & 3)));      // exact
-                }
-            }
-        }
+        for (int e = 0; e < 4; ++e) st.dsc[4 * hg + e][pos] = d * (float)(int)(int8_t)(scw >> (8 * e));   // exact
     };
 
     // Integer stage + fold over the four chunks of one stage (chunk cl = sub-blocks 2cl and
@@ -326,28 +328,16 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
     const int nbase = pcnt / KS, nrem = pcnt % KS;
     const int cnt = nbase + (grp < nrem ? 1 : 0), sb0 = pb0 + grp * nbase + min(grp, nrem);
     const int nst = 2 * cnt, nst_all = 2 * (nbase + (nrem ? 1 : 0));
-    Pre pre;
-    (void)pre;
-    if (nst > 0) {
-        issue_q8(sb0, 0, G.st[0]);
-        if constexpr (!PREP) {
-            load_stage(sb0, 0, pre);
-            commit(pre, sb0, G.st[0]);
-        }
-    }
+    if (nst > 0) issue_stage(sb0, 0, G.st[0]);
     for (int h = 0; h < nst_all; ++h) {
         const int sb = sb0 + (h >> 1), hh = h & 1, cur = h & 1;
         wait_vmem();
         __syncthreads();                    // stage h visible in buffer cur; buffer cur^1 free
-        const bool next = h + 1 < nst;
-        const int sbn = sb0 + ((h + 1) >> 1), hhn = (h + 1) & 1;
-        if (next) {
-            issue_q8(sbn, hhn, G.st[cur ^ 1]);
-            if constexpr (!PREP) load_stage(sbn, hhn, pre);
+        if (h + 1 < nst) issue_stage(sb0 + ((h + 1) >> 1), (h + 1) & 1, G.st[cur ^ 1]);
+        if (h < nst) {
+            if constexpr (!PREP && !ISUMS) decode_dsc(G.st[cur]);
+            compute_stage(sb, hh, G.st[cur]);
         }
-        if (h < nst) compute_stage(sb, hh, G.st[cur]);
-        if constexpr (!PREP)
-            if (next) commit(pre, sbn, G.st[cur ^ 1]);
     }
 
     if constexpr (!ISUMS && KS > 1) {

@@ -222,7 +222,8 @@ def test_calib_library_exports_and_rejects():
         pytest.skip("libqpg_calib.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
     names = re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
-    assert names == ["qpg_calib_mfma_i8", "qpg_calib_step", "qpg_calib_step_blocks", "qpg_probe_mfma"]
+    assert names == ["qpg_calib_mfma_i8", "qpg_calib_step", "qpg_calib_step_blocks", "qpg_probe_mfma",
+                     "qpg_probe_lds_dma"]
     lib = ctypes.CDLL(CALIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -242,7 +243,15 @@ def test_calib_library_exports_and_rejects():
     assert pr(0, None, A16, A16, A16, None) == EINVAL
     assert pr(0, A8, A16, A16, A16, None) == EALIGN
     assert pr(2, A16, A16, A8, A16, None) == EALIGN
+    dm = lib.qpg_probe_lds_dma
+    dm.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    dm.restype = ctypes.c_int
+    assert dm(8, A16, 1024, A16, A16, None) == EINVAL          # width
+    assert dm(4, A16, 0, A16, A16, None) == EINVAL             # nbytes
+    assert dm(4, None, 1024, A16, A16, None) == EINVAL
+    assert dm(16, A8, 1024, A16, A16, None) == EALIGN          # src must be 16-byte aligned
     if not _has_gpu():
+        assert dm(16, A16, 1024, A16, A16, None) == EDEVICE
         assert st(2, 3, 100, A16, None) == EDEVICE
         assert pr(1, A8, A8, A16, A16, None) == EDEVICE     # 8-byte operands suffice for kind 1
     f = lib.qpg_calib_mfma_i8

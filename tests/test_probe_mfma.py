@@ -9,6 +9,11 @@
 * The accumulator trick of the fold: an int32 product accumulated onto the bits of 1.5 * 2^23
   reads as the f32 value 1.5 * 2^23 + I exactly, at the largest |I| each weight format
   reaches (15 * 127 * 32 for q4_K, 32 * 127 * 16 for q6_K).
+* LDS-direct loads (buffer_load_dword[x4] with the LDS flag), which stage every tile: lane L's
+  4 / 16 bytes land at LDS byte 4 L / 16 L, each lane's own source offset is honoured --
+  permutations, and offsets that are not multiples of 4 (the raw q6_K staging reads rows that
+  start 2 bytes past a 4-byte boundary) -- and bytes past the descriptor's range read as zero
+  (rows and tokens past the matrix).
 """
 import ctypes
 import os
@@ -136,3 +141,40 @@ def test_step_probe_runs():
             torch.cuda.synchronize()
             v = out.view(nb, 4).cpu().numpy()
             assert (v[:, 0] > 0).all() and (v[:, 1] > 0).all() and (v[:, 3] == 0).all()
+
+
+def test_lds_direct_loads():
+    lib = ctypes.CDLL(CALIB)
+    f = lib.qpg_probe_lds_dma
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    src_np = ((np.arange(2048) * 7 + 3) & 255).astype(np.uint8)
+    src = torch.from_numpy(src_np).to(DEV)
+
+    def run(width, voff, nbytes):
+        v = torch.tensor(voff, dtype=torch.int32, device=DEV)
+        out = torch.zeros(256, dtype=torch.int32, device=DEV)
+        assert f(width, src.data_ptr(), nbytes, v.data_ptr(), out.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        return out.cpu().numpy().view(np.uint8)
+
+    def expect(width, voff, nbytes):
+        e = np.frombuffer(np.full(256, 0xDEADBEEF, np.uint32).tobytes(), np.uint8).copy()
+        for lane, o in enumerate(voff):
+            for b in range(width):
+                e[width * lane + b] = src_np[o + b] if o + b < nbytes else 0
+        return e
+
+    cases = [(4, [4 * l for l in range(64)], 2048),                    # identity
+             (4, [4 * ((l * 37) % 64) for l in range(64)], 2048),      # a permutation of dwords
+             (16, [16 * ((l * 29) % 64) for l in range(64)], 2048),    # a permutation of granules
+             (4, [4 * l + 2 for l in range(64)], 2048),                # 2 bytes past 4-byte boundaries
+             (4, [4 * l + 1 for l in range(64)], 2048),
+             (16, [16 * l + 2 for l in range(64)], 2048),
+             (16, [16 * l + 6 for l in range(64)], 2048),
+             (16, [16 * l for l in range(64)], 100),                   # past the range: zeros
+             # raw q6_K rows: 8 rows of 210-byte blocks, 8 dwords each from byte 2 of the row
+             (4, [(l >> 3) * 210 + 2 + 4 * (l & 7) for l in range(64)], 2048)]
+    for width, voff, nbytes in cases:
+        got = run(width, voff, nbytes)
+        assert np.array_equal(got, expect(width, voff, nbytes)), (width, voff[:3], nbytes)
