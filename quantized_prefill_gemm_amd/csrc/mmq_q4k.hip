@@ -35,12 +35,12 @@
 //    MFMAs are issued one step ahead of the fold that consumes them, so the matrix core
 //    runs while the VALU folds the previous result.
 //  * Min term: per super-block, sum_s m_js * (da*ssum)_is is a K=8 product. m (0..63) is
-//    exact in bf16; da*ssum is an exact f32 (11 + 12 significant bits) split into three
-//    bf16 pieces that sum to it exactly. Two v_mfma_f32_32x32x16_bf16 (pieces x1|x2 in the
-//    two k-groups, then x3 with the second group zeroed) give R with f32 accumulation, and
-//    one FMA with -dmin per output and super-block folds it into y. (On gfx950 matrix-core
-//    and VALU time add up, so this two-MFMA form is cheaper than carrying -dmin*m through
-//    more MFMAs.)
+//    exact in bf16; da*ssum (an exact f32 of up to 23 significant bits) enters as two bf16
+//    pieces, its top 8 bits (truncation) and the remainder rounded to nearest, which sum to
+//    it within 2^-16 of its magnitude (exactly when it has at most 16 significant bits). One
+//    v_mfma_f32_32x32x16_bf16 per token sub-tile (pieces x1 | x2 in the two k-groups against
+//    m | m) gives R with f32 accumulation, and one FMA with -dmin per output and super-block
+//    folds it into y.
 //  * The "isums" instantiation runs the same staging, unpack and MFMA code and stores the
 //    integer sums instead of folding them (the bit-exact witness of the integer stage).
 #include "qpg_common.h"
@@ -54,7 +54,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int TM = 64;            // tokens per workgroup tile
 constexpr int TN = 128;           // weight rows per workgroup tile
-constexpr int PC_STRIDE = 24;     // bf16 per token: three pieces x 8 sub-blocks
+constexpr int PC_STRIDE = 16;     // bf16 per token: two pieces x 8 sub-blocks
 constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
 
 // LDS of one group of four waves (one K range of the tile). Stage-buffer layouts, in
@@ -75,7 +75,7 @@ struct GroupLds {
     alignas(16) uint16_t bw[TN * 8];         // m per row and sub-block as bf16
     alignas(16) float bnd[TN];               // -dmin per row, rows in C-register order per wave
 };
-static_assert(sizeof(GroupLds) == 46592, "LDS of one group");
+static_assert(sizeof(GroupLds) == 45568, "LDS of one group");
 static_assert(4 * (AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= TM * TN * 4, "a group's stage buffers hold its partial tile");
 
 
@@ -244,11 +244,10 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
                                   (mb[4] >> 16) | (mb[5] & 0xFFFF0000u), (mb[6] >> 16) | (mb[7] & 0xFFFF0000u)};
             *reinterpret_cast<uint32x4*>(L.bw + j * 8) = mw4;
         } else {
-            // per chunk: da, -1.5*2^23*da, and da*ssum split into three bf16 pieces by
-            // truncation (each piece keeps the top 8 significant bits of what is left; 24 bits
-            // in, so the third remainder is itself a bf16 and the pieces sum exactly)
+            // per chunk: da, -1.5*2^23*da, and da*ssum as two bf16 pieces: its top 8 significant
+            // bits by truncation, then the (exact) remainder rounded to nearest
             const int u = tid - TN, t = u >> 1, c4 = 4 * (u & 1);
-            uint32_t p1[4], p2[4], p3[4];
+            uint32_t p1[4], p2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t hw = hv[e];
@@ -257,16 +256,12 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
                 const float v = da * (float)(int)(int16_t)(hw >> 16);       // da*ssum exact (23 bits)
                 const float b1 = __uint_as_float(__float_as_uint(v) & 0xFFFF0000u);
                 const float r1 = v - b1;                                     // exact
-                const float b2 = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-                const float r2 = r1 - b2;                                    // exact, <= 8 significant bits
                 p1[e] = __float_as_uint(b1);
-                p2[e] = __float_as_uint(b2);
-                p3[e] = __float_as_uint(r2);
+                p2[e] = f32_to_bf16_bits(r1) << 16;                          // |r1 - p2| <= 2^-16 |v|
             }
             uint16_t* axr = L.ax + t * PC_STRIDE + c4;
             *reinterpret_cast<uint32x2*>(axr) = uint32x2{(p1[0] >> 16) | (p1[1] & 0xFFFF0000u), (p1[2] >> 16) | (p1[3] & 0xFFFF0000u)};
             *reinterpret_cast<uint32x2*>(axr + 8) = uint32x2{(p2[0] >> 16) | (p2[1] & 0xFFFF0000u), (p2[2] >> 16) | (p2[3] & 0xFFFF0000u)};
-            *reinterpret_cast<uint32x2*>(axr + 16) = uint32x2{(p3[0] >> 16) | (p3[1] & 0xFFFF0000u), (p3[2] >> 16) | (p3[3] & 0xFFFF0000u)};
         }
     };
 
@@ -337,17 +332,12 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
         asm volatile("" : "+v"(y[0]), "+v"(y[1]));
     };
 
-    // Min term of one super-block: R = sum_s m_s * (x1 + x2 + x3)_s on the matrix core, then
-    // y += -dmin * R. MFMA 1 pairs x1 (k-group 0) and x2 (k-group 1) with m, MFMA 2 pairs x3
-    // with m in k-group 0 only.
+    // Min term of one super-block: R = sum_s m_s * (x1 + x2)_s on the matrix core (x1 in
+    // k-group 0, x2 in k-group 1, both against m), then y += -dmin * R.
     auto min_term = [&]() {
         const uint16_t* bwr = L.bw + wr * 8;            // m of this lane's weight row
-        bf16x8 mA, mA2;
+        bf16x8 mA;
         __builtin_memcpy(&mA, bwr, 16);
-        const int32x4 z4 = {0, 0, 0, 0};
-        int32x4 mraw; __builtin_memcpy(&mraw, bwr, 16);
-        const int32x4 mraw2 = hg ? z4 : mraw;
-        __builtin_memcpy(&mA2, &mraw2, 16);
         floatx4 ndv[4];
         const floatx4* ndp = reinterpret_cast<const floatx4*>(&L.bnd[32 * wave + 16 * hg]);
 #pragma unroll
@@ -355,12 +345,10 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
 #pragma unroll
         for (int ts = 0; ts < 2; ++ts) {
             const uint16_t* axr = L.ax + (32 * ts + l32) * PC_STRIDE;
-            bf16x8 x12, x3;
+            bf16x8 x12;
             __builtin_memcpy(&x12, axr + 8 * hg, 16);
-            __builtin_memcpy(&x3, axr + 16, 16);
             floatx16 R = {};
             R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA, x12, R, 0, 0, 0);
-            R = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mA2, x3, R, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 16; ++r) y[ts][r] = fmaf(R[r], ndv[r >> 2][r & 3], y[ts][r]);
         }
