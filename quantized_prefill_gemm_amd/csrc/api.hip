@@ -39,8 +39,8 @@ int check_mmq_shape(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || N < 1 || K < 256 || K % 256 != 0) return QPG_EINVAL;
     if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return QPG_EINVAL;
-    // tile counts must fit one grid dimension
-    const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
+    // tile counts must fit one grid dimension (counted at the smallest tile, 32 x 128)
+    const int64_t tiles = ((M + 31) / 32) * ((N + 127) / 128);
     if (tiles >= kMaxDim) return QPG_EINVAL;
     return QPG_OK;
 }
@@ -155,15 +155,16 @@ int mmq_exp_checked(const void* we, const void* xq, float* y, int32_t* s, int64_
 // workgroup per CU.
 constexpr int kSkMaxPieces = 8;
 
-int64_t form_tiles(int form, int64_t M, int64_t N)
+int64_t form_tiles(int form, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t tn = form == 3 ? 64 : 128;                  // expanded q6_K uses 64-row tiles
-    return ((M + 63) / 64) * ((N + tn - 1) / tn);
+    const int64_t tm = form == 0 ? qpg_q4K_tile_m(M, N, K) : 64;   // the q4_K kernel's tile height per shape
+    const int64_t tn = form == 3 ? 64 : 128;                        // expanded q6_K uses 64-row tiles
+    return ((M + tm - 1) / tm) * ((N + tn - 1) / tn);
 }
 
 int sk_pieces(int form, int64_t M, int64_t N, int64_t K)
 {
-    const int64_t tiles = form_tiles(form, M, N);
+    const int64_t tiles = form_tiles(form, M, N, K);
     if (tiles > 128) return 1;
     int64_t p = 256 / tiles;
     p = p < kSkMaxPieces ? p : kSkMaxPieces;
@@ -176,7 +177,7 @@ bool form_shape_ok(int form, int64_t M, int64_t N, int64_t K)
 {
     if (check_mmq_shape(M, N, K) != QPG_OK) return false;
     if (form == 2) return prep_shape_ok(N, K);
-    if (form == 3) return exp_shape_ok(N, K) && form_tiles(3, M, N) < kMaxDim;
+    if (form == 3) return exp_shape_ok(N, K) && form_tiles(3, M, N, K) < kMaxDim;
     return form >= 0 && form <= 1;
 }
 

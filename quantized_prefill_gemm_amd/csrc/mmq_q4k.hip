@@ -52,7 +52,6 @@ typedef unsigned uint32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned uint32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int TM = 64;            // tokens per workgroup tile
 constexpr int TN = 128;           // weight rows per workgroup tile
 constexpr int PC_STRIDE = 16;     // bf16 per token: two pieces x 8 sub-blocks
 constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
@@ -63,8 +62,12 @@ constexpr int HALF = 128;         // k per pipeline stage (half a super-block)
 // permutation is applied by the LDS-direct loads' per-lane source offsets):
 //   q8 tile: token t, granule g (k 16g..16g+15 of the half) at slot 8t + (g ^ ((t >> 1) & 7))
 //   raw qs:  row j, granule g (qs bytes 16g.. of the half)   at slot 4j + (g ^ ((j >> 2) & 3))
-constexpr int AQ_SLOTS = TM * 8, BQ_SLOTS = TN * 4;          // 512 each: 8 slabs of 64
+// TS = token sub-tiles of 32 per wave: the workgroup tile is TM = 32*TS tokens x 128 rows
+// (TS = 2 for long prompts, TS = 1 halves the token padding of short ones).
+constexpr int BQ_SLOTS = TN * 4;                                  // raw qs: 8 slabs of 64
+template <int TS>
 struct GroupLds {
+    static constexpr int TM = 32 * TS, AQ_SLOTS = TM * 8;         // q8 tile: 4*TS slabs of 64
     alignas(16) uint8_t aq0[AQ_SLOTS * 16];
     alignas(16) uint8_t aq1[AQ_SLOTS * 16];
     alignas(16) uint8_t bq0[BQ_SLOTS * 16];
@@ -75,8 +78,10 @@ struct GroupLds {
     alignas(16) uint16_t bw[TN * 8];         // m per row and sub-block as bf16
     alignas(16) float bnd[TN];               // -dmin per row, rows in C-register order per wave
 };
-static_assert(sizeof(GroupLds) == 45568, "LDS of one group");
-static_assert(4 * (AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= TM * TN * 4, "a group's stage buffers hold its partial tile");
+static_assert(sizeof(GroupLds<2>) == 45568 && sizeof(GroupLds<1>) == 34304, "LDS of one group");
+static_assert(4 * (GroupLds<1>::AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= 32 * TN * 4 &&
+                  4 * (GroupLds<2>::AQ_SLOTS + BQ_SLOTS) * 16 / 2 >= 64 * TN * 4,
+              "a group's stage buffers hold its partial tile");
 
 
 __device__ __forceinline__ void tile_coords(int& m_tile, int& n_tile, int& piece, int tiles_m, int total,
@@ -118,7 +123,7 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, void* lds_w
 
 // KS = number of four-wave groups per workgroup; group g computes the tile over its own
 // contiguous range of super-blocks and the partial sums are added in group order at the end.
-template <bool ISUMS, int KS>
+template <bool ISUMS, int KS, int TS>
 __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const uint8_t* __restrict__ W,
                                                          const int8_t* __restrict__ qplane,
                                                          const uint32_t* __restrict__ hdr,
@@ -126,14 +131,15 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
                                                          int32_t* __restrict__ S,
                                                          int M, int N, int K, int tiles_m, int total, int pieces)
 {
-    __shared__ GroupLds lds_all[KS];
+    constexpr int TM = 32 * TS;
+    __shared__ GroupLds<TS> lds_all[KS];
     int m_tile, n_tile, piece;
     tile_coords(m_tile, n_tile, piece, tiles_m, total, pieces);
     // K-split over workgroups (few tiles): piece p adds the super-blocks [p*nsb/P, (p+1)*nsb/P)
     // and writes its partial tile to Y + p*M*N (a workspace the caller sums in piece order).
     if (pieces > 1) Y += (size_t)piece * M * N;
     const int grp = KS > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 8) : 0;
-    GroupLds& L = lds_all[grp];
+    GroupLds<TS>& L = lds_all[grp];
     const int tid = threadIdx.x & 255, lane = tid & 63;        // thread index inside the group
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hg = lane >> 5, l32 = lane & 31;
@@ -153,14 +159,18 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
 
     // Per-lane source offsets of the LDS-direct loads. A slab is 64 consecutive slots
     // (1 KiB) written by one wave instruction, lane L to slot 64*slab + L; the lane fetches
-    // the granule that the permutation puts there. The q8 tile and the raw qs have 8 slabs
-    // each, wave w loads slabs w and w + 4 of both. Stage offsets are added per load.
-    unsigned voA[2], voB[2];
+    // the granule that the permutation puts there. The q8 tile has 4*TS slabs, the raw qs 8;
+    // wave w loads slabs w, w + 4, ... of both. Stage offsets are added per load.
+    unsigned voA[TS], voB[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < TS; ++i) {
         const int sl = 64 * (wave + 4 * i) + lane;
         const int t = sl >> 3, ga = (sl & 7) ^ ((t >> 1) & 7);
         voA[i] = (unsigned)(t * K + 16 * ga);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int sl = 64 * (wave + 4 * i) + lane;
         const int j = sl >> 2, gb = (sl & 3) ^ ((j >> 2) & 3);
         voB[i] = (unsigned)(j * wrow + 16 + 16 * gb);
     }
@@ -179,14 +189,15 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
             __builtin_amdgcn_make_buffer_rsrc((void*)(wbase + ob), 0, (int)(nW - ob), 0x00020000);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            lds_load16(rQs, aq + 1024 * (wave + 4 * i), (int)voA[i]);
+            if (i < TS) lds_load16(rQs, aq + 1024 * (wave + 4 * i), (int)voA[i]);
             lds_load16(rWs, bq + 1024 * (wave + 4 * i), (int)voB[i]);
         }
     };
 
     // Block headers of one super-block, one 16-byte load per thread into registers:
     // threads 0..127 the q4_K header (d, dmin, 12 scale bytes) of row tid, threads
-    // 128..255 four q8_1 words (token (tid-128)/2, chunks 4*(tid&1)..+3).
+    // 128..255 four q8_1 words (token (tid-128)/2, chunks 4*(tid&1)..+3; with TM = 32 the
+    // threads of tokens 32..63 load past the tile's rows, i.e. zeros, and decode nothing).
     auto load_headers = [&](int sb) -> uint32x4 {
         int32x4 v;
         if (tid < TN)
@@ -201,9 +212,9 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
     int32x16 magic;
 #pragma unroll
     for (int r = 0; r < 16; ++r) magic[r] = MAGIC_BITS;
-    floatx16 y[2];
+    floatx16 y[TS];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < TS; ++a)
 #pragma unroll
         for (int r = 0; r < 16; ++r) y[a][r] = 0.0f;
 
@@ -243,7 +254,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
             const uint32x4 mw4 = {(mb[0] >> 16) | (mb[1] & 0xFFFF0000u), (mb[2] >> 16) | (mb[3] & 0xFFFF0000u),
                                   (mb[4] >> 16) | (mb[5] & 0xFFFF0000u), (mb[6] >> 16) | (mb[7] & 0xFFFF0000u)};
             *reinterpret_cast<uint32x4*>(L.bw + j * 8) = mw4;
-        } else {
+        } else if (((tid - TN) >> 1) < TM) {
             // per chunk: da, -1.5*2^23*da, and da*ssum as two bf16 pieces: its top 8 significant
             // bits by truncation, then the (exact) remainder rounded to nearest
             const int u = tid - TN, t = u >> 1, c4 = 4 * (u & 1);
@@ -266,7 +277,8 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
     };
 
     // Integer stage + fold over the four chunks of one half super-block, MFMA one step
-    // ahead of the fold. Step k = 0..7 is (chunk c = 4*hh + k/2, token sub-tile k%2).
+    // ahead of the fold. Step k = 0..4*TS-1 is (chunk c = 4*hh + k/TS, token sub-tile k%TS);
+    // one 16-byte read of raw qs serves 2*TS steps (two chunks).
     auto compute_stage = [&](int sb, int hh, const uint8_t* aq, const uint8_t* bq) {
         auto a_from = [&](const uint32x4& raw, int c) -> int32x4 {
             const uint32x4 u = (c & 1) ? ((raw >> 4u) & 0x0F0F0F0Fu) : (raw & 0x0F0F0F0Fu);
@@ -281,17 +293,18 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
             return *reinterpret_cast<const int32x4*>(aq + aq_off[cl] + 4096 * ts);
         };
         if constexpr (!ISUMS) asm volatile("" : "+v"(magic));   // keep the constant in VGPRs
+        constexpr int NSTEP = 4 * TS;
         uint32x4 raw = ld_raw(0);
         int32x16 F[2];
         F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, 0), ld_b(0, 0), magic, 0, 0, 0);
         floatx4 dsv[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int cl = k >> 1, ts = k & 1, c = 4 * hh + cl;
-            const int k1 = k + 1, cl1 = k1 >> 1, ts1 = k1 & 1;
+        for (int k = 0; k < NSTEP; ++k) {
+            const int cl = k / TS, ts = k % TS, c = 4 * hh + cl;
+            const int k1 = k + 1, cl1 = k1 / TS, ts1 = k1 % TS;
             int32x4 bn;
-            if (k1 < 8) {
-                if ((k1 & 3) == 0) raw = ld_raw(k1 >> 2);
+            if (k1 < NSTEP) {
+                if ((k1 % (2 * TS)) == 0) raw = ld_raw(k1 / (2 * TS));
                 bn = ld_b(cl1, ts1);
             }
             if constexpr (!ISUMS) {
@@ -302,7 +315,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (k1 < 8)
+            if (k1 < NSTEP)
                 F[k1 & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a_from(raw, cl1), bn, magic, 0, 0, 0);
             const int32x16 Fk = F[k & 1];
             if constexpr (ISUMS) {
@@ -328,8 +341,9 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
             __builtin_amdgcn_sched_barrier(0);
         }
         // The folds of this stage are done here: without the pin, they may be sunk past the
-        // next barrier, which keeps all eight MFMA results live at once.
-        asm volatile("" : "+v"(y[0]), "+v"(y[1]));
+        // next barrier, which keeps all the stage's MFMA results live at once.
+#pragma unroll
+        for (int ts = 0; ts < TS; ++ts) asm volatile("" : "+v"(y[ts]));
     };
 
     // Min term of one super-block: R = sum_s m_s * (x1 + x2)_s on the matrix core (x1 in
@@ -343,7 +357,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) ndv[q4] = ndp[q4];
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
+        for (int ts = 0; ts < TS; ++ts) {
             const uint16_t* axr = L.ax + (32 * ts + l32) * PC_STRIDE;
             bf16x8 x12;
             __builtin_memcpy(&x12, axr + 8 * hg, 16);
@@ -410,7 +424,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
         if (grp > 0) {
             floatx4* red = reinterpret_cast<floatx4*>(L.aq0);
 #pragma unroll
-            for (int ts = 0; ts < 2; ++ts)
+            for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     red[(4 * ts + q) * 256 + tid] = floatx4{y[ts][4 * q], y[ts][4 * q + 1], y[ts][4 * q + 2], y[ts][4 * q + 3]};
@@ -421,7 +435,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
         for (int g2 = 1; g2 < KS; ++g2) {
             const floatx4* red = reinterpret_cast<const floatx4*>(lds_all[g2].aq0);
 #pragma unroll
-            for (int ts = 0; ts < 2; ++ts)
+            for (int ts = 0; ts < TS; ++ts)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const floatx4 p = red[(4 * ts + q) * 256 + tid];
@@ -436,7 +450,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
         // consecutive weight rows n0 + 32*wave + 8b + 4hg + 0..3
         const bool vec = ((N & 3) == 0) && ((((uintptr_t)Y) & 15) == 0);
 #pragma unroll
-        for (int ts = 0; ts < 2; ++ts) {
+        for (int ts = 0; ts < TS; ++ts) {
             const int tok = m0 + 32 * ts + l32;
             if (tok >= M) continue;
             float* yrow = Y + (size_t)tok * N;
@@ -459,34 +473,44 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q4K_kernel(const
 }  // namespace q4k
 }  // namespace qpg
 
-hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
-                              int64_t K, int pieces, hipStream_t s)
+namespace {
+template <int TS>
+hipError_t launch_q4K(const uint8_t* wb, const int8_t* qplane, const uint32_t* hdr, float* y, int32_t* isums,
+                      int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s)
 {
     using namespace qpg::q4k;
-    const int tiles_m = (int)((M + TM - 1) / TM);
+    const int tiles_m = (int)((M + 32 * TS - 1) / (32 * TS));
     const int tiles_n = (int)((N + TN - 1) / TN);
     const int total = tiles_m * tiles_n;
-    const int8_t* qplane = static_cast<const int8_t*>(xq);
-    const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
-    const uint8_t* wb = static_cast<const uint8_t*>(w);
     // At most one tile per CU (256 CUs): split each tile's super-blocks over three
     // four-wave groups, so each SIMD still holds three waves.
     const bool split = total * pieces <= 256 && (K / 256) / pieces >= 3;
     const unsigned grid = (unsigned)(total * pieces);
     if (isums) {
         if (split)
-            hipLaunchKernelGGL((mmq_q4K_kernel<true, 3>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 3, TS>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
                                (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q4K_kernel<true, 1>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+            hipLaunchKernelGGL((mmq_q4K_kernel<true, 1, TS>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
                                (int)M, (int)N, (int)K, tiles_m, total, pieces);
     } else {
         if (split)
-            hipLaunchKernelGGL((mmq_q4K_kernel<false, 3>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 3, TS>), dim3(grid), dim3(768), 0, s, wb, qplane, hdr, y, isums,
                                (int)M, (int)N, (int)K, tiles_m, total, pieces);
         else
-            hipLaunchKernelGGL((mmq_q4K_kernel<false, 1>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
+            hipLaunchKernelGGL((mmq_q4K_kernel<false, 1, TS>), dim3(grid), dim3(256), 0, s, wb, qplane, hdr, y, isums,
                                (int)M, (int)N, (int)K, tiles_m, total, pieces);
     }
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t qpg_launch_mmq_q4K(const void* w, const void* xq, float* y, int32_t* isums, int64_t M, int64_t N,
+                              int64_t K, int pieces, hipStream_t s)
+{
+    const int8_t* qplane = static_cast<const int8_t*>(xq);
+    const uint32_t* hdr = reinterpret_cast<const uint32_t*>(qplane + M * K);
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    return qpg_q4K_tile_m(M, N, K) == 32 ? launch_q4K<1>(wb, qplane, hdr, y, isums, M, N, K, pieces, s)
+                                         : launch_q4K<2>(wb, qplane, hdr, y, isums, M, N, K, pieces, s);
 }

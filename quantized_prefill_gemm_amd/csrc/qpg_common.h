@@ -17,6 +17,8 @@ constexpr int QK8 = 32;          // values per q8_1 block (one "chunk" of K)
 constexpr int Q4K_BYTES = 144;
 constexpr int Q6K_BYTES = 210;
 
+
+
 // Bits of the f32 value 1.5 * 2^23. An integer |v| < 2^22 added to these bits gives the
 // bits of the f32 value 1.5*2^23 + v exactly (all such values share one exponent and
 // unit spacing), so an int32 MFMA accumulating onto this constant delivers its integer
@@ -47,6 +49,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 }  // namespace qpg
+
+// Token-tile height of the q4_K kernel for a shape (the launcher and the split-K piece count
+// both use this): 32 tokens (one 32-token sub-tile per wave) or 64. With t64 = the number of
+// 64 x 128 tiles, 32-token tiles are taken when t64 <= 128 (too few tiles for 256 CUs: halving
+// the tile doubles them and halves the token padding of a short prompt) or when M <= 256 and
+// t64 > 256 (more workgroups per CU at four waves per SIMD); 64 otherwise. Measured on the 7B
+// layer shapes (split-K entry, interleaved A/B): 4096 x 4096 at M = 16, 32, 64, 128, 256:
+// 1.18, 1.23, 1.14, 1.23, 1.05x; 11008 x 4096 at M = 16, 32, 64, 256: 1.30, 1.28, 1.09, 1.08x,
+// and 0.92x at M = 128 (172 tiles), which keeps 64.
+inline int qpg_q4K_tile_m(int64_t M, int64_t N, int64_t K)
+{
+    (void)K;
+    const int64_t t64 = ((M + 63) / 64) * ((N + 127) / 128);
+    return (t64 <= 128 || (M <= 256 && t64 > 256)) ? 32 : 64;
+}
 
 // Kernel launchers (defined in the .hip files; called by the C ABI layer after the
 // arguments have been validated). They return hipGetLastError() of the launch.

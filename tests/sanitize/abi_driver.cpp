@@ -45,12 +45,12 @@ int main(int argc, char** argv)
     CHECK(q6K_expand(A16, nullptr, 64, 256, nullptr) == QPG_EINVAL);
     CHECK(mmq_q6K_exp_q8(A16, A16, F16, 64, 256, 1 << 24, nullptr) == QPG_EINVAL);
     CHECK(mmq_q6K_exp_csums(A16, A16, static_cast<int32_t*>(A2), 64, 256, 256, nullptr) == QPG_EALIGN);
-    const size_t need = qpg_mmq_sk_bytes(512, 512, 4096, 0);
-    CHECK(need == 5u * 512u * 512u * 4u);
+    const size_t need = qpg_mmq_sk_bytes(512, 512, 4096, 0), need6 = qpg_mmq_sk_bytes(512, 512, 4096, 1);
+    CHECK(need == 4u * 512u * 512u * 4u && need6 == 5u * 512u * 512u * 4u);
     CHECK(mmq_q4K_q8_sk(A16, A16, F16, 512, 512, 4096, A16, need - 4, nullptr) == QPG_EINVAL);
-    CHECK(mmq_q6K_q8_sk(A16, A16, F16, 512, 512, 4096, A8, need, nullptr) == QPG_EALIGN);
-    CHECK(mmq_q6K_prep_q8_sk(A16, A16, F16, 512, 512, 288, A16, need, nullptr) == QPG_EINVAL);
-    CHECK(mmq_q6K_exp_q8_sk(nullptr, A16, F16, 512, 512, 4096, A16, need, nullptr) == QPG_EINVAL);
+    CHECK(mmq_q6K_q8_sk(A16, A16, F16, 512, 512, 4096, A8, need6, nullptr) == QPG_EALIGN);
+    CHECK(mmq_q6K_prep_q8_sk(A16, A16, F16, 512, 512, 288, A16, need6, nullptr) == QPG_EINVAL);
+    CHECK(mmq_q6K_exp_q8_sk(nullptr, A16, F16, 512, 512, 4096, A16, need6, nullptr) == QPG_EINVAL);
     CHECK(mmq_q4K_noalloc(A16, F16, F16, 2711, 256, 11008, nullptr) == QPG_ESCRATCH);
     CHECK(mmq_q4K_noalloc(A8, F16, F16, 64, 256, 256, nullptr) == QPG_EALIGN);
     CHECK(qpg_calib_mfma_i8(0, 10, static_cast<uint64_t*>(A16), nullptr) == -1);

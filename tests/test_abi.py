@@ -161,9 +161,12 @@ def test_q6K_expand_sizes_and_rejects(L):
 
 
 def test_splitk_workspace_sizes(L):
-    # P = min(8, 256 // tiles, (K/256) // 3) when tiles <= 128, else no split (0 bytes)
-    assert L.qpg_mmq_sk_bytes(512, 512, 4096, 0) == 5 * 512 * 512 * 4      # 32 tiles, 16 SB -> 5
-    assert L.qpg_mmq_sk_bytes(512, 1376, 4096, 0) == 2 * 512 * 1376 * 4    # 88 tiles -> 2
+    # P = min(8, 256 // tiles, (K/256) // 3) when tiles <= 128, else no split (0 bytes); q4_K
+    # tiles are 32 x 128 when the 64 x 128 grid has <= 128 tiles (or M <= 256 and > 256 tiles)
+    assert L.qpg_mmq_sk_bytes(512, 512, 4096, 0) == 4 * 512 * 512 * 4      # 64 tiles of 32 rows -> 4
+    assert L.qpg_mmq_sk_bytes(512, 1376, 4096, 0) == 0                     # 176 tiles of 32 rows
+    assert L.qpg_mmq_sk_bytes(16, 4096, 4096, 0) == 5 * 16 * 4096 * 4      # 32 tiles of 32 rows -> 5
+    assert L.qpg_mmq_sk_bytes(512, 512, 4096, 1) == 5 * 512 * 512 * 4      # q6_K: 32 tiles of 64 rows -> 5
     assert L.qpg_mmq_sk_bytes(512, 512, 11008, 1) == 8 * 512 * 512 * 4     # 32 tiles, 43 SB -> 8
     assert L.qpg_mmq_sk_bytes(512, 512, 11008, 2) == 8 * 512 * 512 * 4
     assert L.qpg_mmq_sk_bytes(512, 512, 11008, 3) == 4 * 512 * 512 * 4     # 64 tiles of 64 x 64 -> 4
@@ -180,11 +183,13 @@ def test_splitk_workspace_sizes(L):
 
 def test_splitk_rejects(L):
     need = L.qpg_mmq_sk_bytes(512, 512, 4096, 0)
+    need6 = L.qpg_mmq_sk_bytes(512, 512, 4096, 1)
+    assert need > 0 and need6 > 0
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, None, need, None) == EINVAL      # no workspace
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A16, need - 4, None) == EINVAL  # too small
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A8, need, None) == EALIGN
     assert L.mmq_q4K_q8_sk(A8, A16, A16, 512, 512, 4096, A16, need, None) == EALIGN
-    assert L.mmq_q6K_q8_sk(A2, A16, A16, 512, 512, 4096, A16, need, None) == EALIGN       # q6_K: 4 bytes
+    assert L.mmq_q6K_q8_sk(A2, A16, A16, 512, 512, 4096, A16, need6, None) == EALIGN      # q6_K: 4 bytes
     assert L.mmq_q6K_prep_q8_sk(A16, A16, A16, 512, 512, 1 << 24, A16, need, None) == EINVAL
     assert L.mmq_q6K_exp_q8_sk(None, A16, A16, 512, 512, 4096, A16, need, None) == EINVAL
     assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 512, 512, 288, A16, need, None) == EINVAL

@@ -45,14 +45,25 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def q4K_tile_m(M, N):
+    """Token-tile height the q4_K launcher picks (mirror of the library's table): 32 when the
+    64 x 128 grid has <= 128 tiles, or M <= 256 and more than 256 tiles; else 64."""
+    t64 = -(-M // 64) * -(-N // 128)
+    return 32 if (t64 <= 128 or (M <= 256 and t64 > 256)) else 64
+
+
 def launch_form(kind, M, N, K, pieces=1):
     """The tiling the launcher picks (mirrors the launch code): 'split3' = three groups over
-    each tile's super-blocks (<= 256 tiles), 'one-group' / 'eight-wave' otherwise."""
+    each tile's super-blocks (<= 256 tiles), 'one-group' / 'eight-wave' otherwise; q4_K forms
+    carry the token-tile height ('/tm32' for 32-token tiles)."""
     tn = 64 if kind == "exp" else 128
-    tiles = -(-M // 64) * -(-N // tn)
+    tm = q4K_tile_m(M, N) if kind == "q4K" else 64
+    tiles = -(-M // tm) * -(-N // tn)
     if tiles * pieces <= 256 and (K // 256) // pieces >= 3:
-        return "split3"
-    return "eight-wave" if kind == "exp" else "one-group"
+        form = "split3"
+    else:
+        form = "eight-wave" if kind == "exp" else "one-group"
+    return form + ("/tm32" if tm == 32 else "")
 
 
 def quantized(X):
@@ -101,6 +112,31 @@ ISUM_CASES = [
     ("stack down q6_K prepared 1024x4096x11008", ("stack", 6), "prep", "one-group"),
     ("stack down q6_K expanded 1024x4096x11008", ("stack", 6), "exp", "eight-wave"),
 ]
+
+
+def short_prompt(M, N, K, seed):
+    """The workload's distributions (per-token gains) at a short prompt length."""
+    W, X = inputs.small_case("q4_K", M, N, K, seed=seed, gain=True)
+    return "q4_K", M, N, K, W, X
+
+
+SHORT_CASES = [
+    # 32-token q4_K tiles: three-group split (few tiles) and one group per tile (> 256 tiles)
+    ("q4_K 16x4096x4096", (16, 4096, 4096), "split3/tm32"),
+    ("q4_K 128x4096x4096", (128, 4096, 4096), "split3/tm32"),
+    ("q4_K 256x11008x4096", (256, 11008, 4096), "one-group/tm32"),
+]
+
+
+@pytest.mark.parametrize("label,shape,tiling", SHORT_CASES, ids=[c[0] for c in SHORT_CASES])
+def test_integer_stage_full_short_prompts(label, shape, tiling):
+    wtype, M, N, K, W, X = short_prompt(*shape, seed=71)
+    assert launch_form("q4K", M, N, K) == tiling
+    say(f"[integer stage {label}: {tiling}]")
+    xq, q = quantized(X)
+    s = B.mmq_q4K_isums(dev(W.reshape(-1)), xq, M, N, K)
+    torch.cuda.synchronize()
+    compare_slabs(s, lambda t0, t1: O.isums(wtype, W, q[t0:t1]), M, 64, label)
 
 
 @pytest.mark.parametrize("label,src,form,tiling", ISUM_CASES, ids=[c[0] for c in ISUM_CASES])
@@ -225,7 +261,11 @@ EXACT_CASES = [
     ("q4_K 512x11008x4096", "q4K", 512, 11008, 4096, "one-group", None),
     ("q4_K 512x4096x4096", "q4K", 512, 4096, 4096, "split3", None),
     ("q4_K 1024x11008x4096", "q4K", 1024, 11008, 4096, "one-group", None),
-    ("q4_K K-split 512x1376x4096", "q4K", 512, 1376, 4096, "split3", 2),
+    ("q4_K K-split 512x512x4096", "q4K", 512, 512, 4096, "split3/tm32", 4),
+    ("q4_K 512x1376x4096", "q4K", 512, 1376, 4096, "split3/tm32", None),
+    ("q4_K 128x4096x4096", "q4K", 128, 4096, 4096, "split3/tm32", None),
+    ("q4_K 256x11008x4096", "q4K", 256, 11008, 4096, "one-group/tm32", None),
+    ("q4_K K-split 16x4096x4096", "q4K", 16, 4096, 4096, "split3/tm32", 5),
     ("q6_K raw 512x4096x11008", "raw", 512, 4096, 11008, "split3", None),
     ("q6_K raw 1024x4096x11008", "raw", 1024, 4096, 11008, "one-group", None),
     ("q6_K prepared 512x4096x11008", "prep", 512, 4096, 11008, "split3", None),
