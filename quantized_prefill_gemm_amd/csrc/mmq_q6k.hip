@@ -20,19 +20,20 @@
 //  * Staging is a two-deep pipeline of half super-blocks (128 k, one barrier per stage),
 //    all of it by LDS-direct loads issued one stage ahead: the q8 tile by 16-byte loads
 //    (buffer_load_dwordx4 ... lds) in natural order, the q8_1 header words by dword loads,
-//    and the raw weight bytes by dword loads straight into the stage layout below. A lane's
-//    source offset may be any byte offset (rows of 210-byte blocks start only 2-byte
-//    aligned when K/256 is odd), so the per-lane offsets apply the layout's piece swap and
-//    row swizzle during the copy, with no register staging and no shifts. Each wave loads
-//    exactly its own 32 weight rows (and their int8 scales and d), so after its own load
-//    wait it converts their d*sc for the stage without another barrier; the barrier is for
-//    the q8 tile and header words, which every wave reads.
-//  * LDS: inside every 32-byte group of ql and qh the 8-byte pieces 1 and 2 are swapped, so
-//    one 16-byte read gives a lane its 8 bytes of both sub-blocks of a chunk (k-group l>>5
-//    of each K=16 MFMA); the matching q8 operand is two 8-byte reads. Rows are XOR-swizzled
-//    in 16-byte granules so reads of 16 consecutive rows hit 16 bank groups. The prepared
-//    weight form (q6K_prepare) is this stage layout written once to memory, with d*sc
-//    included, staged by plain 16-byte copies.
+//    and the raw weight bytes by 16-byte loads straight from the blocks. A lane's source
+//    offset may be any byte offset (rows of 210-byte blocks start only 2-byte aligned when
+//    K/256 is odd), so rows need no register staging and no shifts; the per-lane offsets
+//    apply the row swizzle. Each wave loads exactly its own 32 weight rows (and their int8
+//    scales and d), so after its own load wait it converts their d*sc for the stage without
+//    another barrier; the barrier is for the q8 tile and header words, which every wave reads.
+//  * LDS: rows of the ql and qh halves XOR-swizzled in 16-byte granules (reads of 16
+//    consecutive rows hit 16 bank groups). A K=16 MFMA wants k-group l>>5 of its sub-block in
+//    lane l: 8 bytes of each of the chunk's two sub-blocks. The prepared form (q6K_prepare:
+//    this stage layout written once to memory, with d*sc included, staged by plain 16-byte
+//    copies) swaps the 8-byte pieces 1 and 2 of every 32-byte group, so one 16-byte read gives
+//    a lane both; on raw blocks the lane halves read the two sub-blocks' granules and
+//    exchange the middle pieces with v_permlane32_swap (two per chunk). The matching q8
+//    operand is two 8-byte reads.
 //  * When the matrix has at most one tile per CU, three groups of four waves share a
 //    workgroup, each over a contiguous range of super-blocks, and the partial tiles are
 //    added in group order through LDS at the end (three waves per SIMD, deterministic).
@@ -171,28 +172,24 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
         const int t = 8 * (2 * wave + i) + (lane >> 3);
         voQ16[i] = t * K + 16 * ((lane & 7) ^ aq_sw(t));
     }
-    // Raw blocks: the stage's bytes go straight into the prepared stage layout by dword
-    // LDS-direct loads whose per-lane source offsets apply the piece swap and the row swizzle
-    // (a lane may read at any byte offset: rows of 210-byte blocks start 2-byte aligned).
-    // LDS dword s of bl is dword dw = s & 3 of slot G = (s >> 2) & 3 of row j = s >> 4; the
-    // slot holds logical granule G ^ bl_sw(j) = 2 g + x, i.e. the ql dwords 8g + 2x, 8g + 2x + 1,
-    // 8g + 4 + 2x, 8g + 5 + 2x of the row's stage half. bh likewise with 8 dwords per row
-    // (qh dwords 2x, 2x + 1, 4 + 2x, 5 + 2x in slot x ^ bh_sw(j)). Slab i = 64 dwords; wave w
-    // loads ql slabs 8w..8w+7 and qh slabs 4w..4w+3, i.e. exactly its own 32 rows, and the
+    // Raw blocks: the stage's bytes go straight into LDS by 16-byte LDS-direct loads (a lane
+    // may read at any byte offset: rows of 210-byte blocks start 2-byte aligned). ql: LDS slot
+    // sl = row sl >> 2, slot sl & 3 holds the row's 16-byte granule (sl & 3) ^ bl_sw(row) of its
+    // stage half; qh: row sl >> 1, granule (sl & 1) ^ bh_sw(row). A slab is 64 slots (1 KiB);
+    // wave w loads ql slabs 2w, 2w + 1 and qh slab w, i.e. exactly its own 32 rows, and the
     // scales and d of those rows.
-    unsigned voL[8], voB[4], voS = 0, voD = 0;
+    unsigned voL[2], voB = 0, voS = 0, voD = 0;
     if constexpr (!PREP) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int sl = 64 * (8 * wave + i) + lane;
-            const int j = sl >> 4, dw = sl & 3, gp = ((sl >> 2) & 3) ^ bl_sw(j);
-            voL[i] = (unsigned)(j * wrow + 4 * (8 * (gp >> 1) + 2 * (gp & 1) + (dw & 1) + 4 * (dw >> 1)));
+        for (int i = 0; i < 2; ++i) {
+            const int sl = 64 * (2 * wave + i) + lane;          // ql slot: row sl >> 2, slot sl & 3
+            const int j = sl >> 2;
+            voL[i] = (unsigned)(j * wrow + 16 * ((sl & 3) ^ bl_sw(j)));
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = 64 * (4 * wave + i) + lane;
-            const int j = sl >> 3, dw = sl & 3, x = ((sl >> 2) & 1) ^ bh_sw(j);
-            voB[i] = (unsigned)(j * wrow + 4 * (2 * x + (dw & 1) + 4 * (dw >> 1)));
+        {
+            const int sl = 64 * wave + lane;                     // qh slot: row sl >> 1, slot sl & 1
+            const int j = sl >> 1;
+            voB = (unsigned)(j * wrow + 16 * ((sl & 1) ^ bh_sw(j)));
         }
         voS = (unsigned)((32 * wave + (lane >> 1)) * wrow + 4 * (lane & 1));
         voD = (unsigned)((32 * wave + (lane & 31)) * wrow);
@@ -218,9 +215,8 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
             const unsigned blk = (unsigned)(sb * Q6K_BYTES);
             const __amdgpu_buffer_rsrc_t rL = wdesc(blk + 64 * hh), rB = wdesc(blk + 128 + 32 * hh);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) lds_load4(rL, st.bl + 256 * (8 * wave + i), (int)voL[i]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lds_load4(rB, st.bh + 256 * (4 * wave + i), (int)voB[i]);
+            for (int i = 0; i < 2; ++i) lds_load16(rL, st.bl + 1024 * (2 * wave + i), (int)voL[i]);
+            lds_load16(rB, st.bh + 1024 * wave, (int)voB);
             if constexpr (!ISUMS) {
                 lds_load4(wdesc(blk + 192 + 8 * hh), &st.wsc[wave][0], (int)voS);
                 if (lane < 32) lds_load4(wdesc(blk + 206), &st.wd[wave][0], (int)voD);
@@ -270,6 +266,17 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
                 // q6 = lo + hi <= 63 per byte; q6 + 96 <= 159 never carries into the next byte,
                 // and (q6 + 96) ^ 0x80 is the signed byte q6 - 32
                 v[e] = (lo + hi + 0x60606060u) ^ 0x80808080u;
+            }
+            if constexpr (!PREP) {
+                // raw order: lane half hg holds all 16 bytes of sub-block 2cl + hg; exchange the
+                // middle 8-byte pieces between the halves (upper half's dwords 0-1 <-> lower
+                // half's dwords 2-3), so each half holds its k-group of both sub-blocks
+                const auto s0 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+                v[0] = s0[0];
+                v[2] = s0[1];
+                v[1] = s1[0];
+                v[3] = s1[1];
             }
             const long a0 = (long)(((unsigned long)v[1] << 32) | v[0]);      // sub-block 2cl, k-group hg
             const long a1 = (long)(((unsigned long)v[3] << 32) | v[2]);      // sub-block 2cl+1
