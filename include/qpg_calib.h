@@ -65,6 +65,14 @@ int qpg_probe_mfma(int kind, const void* a, const void* b, const void* c, void* 
  * nbytes outside [1, 2^30]), -2 (alignment), -3 (launch error) or -4 (not gfx950). */
 int qpg_probe_lds_dma(int width, const void* src, int64_t nbytes, const int32_t* voff, uint32_t* out, void* stream);
 
+/* v_permlane32_swap probe (the raw q6_K kernel exchanges operand pieces between the wave's
+ * lane halves with it): one wave loads register a from in[0..63] and b from in[64..127]
+ * (lane l: in[l], in[64 + l]), executes the swap, and writes a to out[0..63] and b to
+ * out[64..127]. Device pointers owned by the caller, 4-byte aligned. Asynchronous on
+ * `stream`. Returns 0, -1 (null pointer), -2 (alignment), -3 (launch error) or -4 (not
+ * gfx950). */
+int qpg_probe_permlane32_swap(const uint32_t* in, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -119,3 +119,26 @@ extern "C" int qpg_probe_lds_dma(int width, const void* src, int64_t nbytes, con
                            (int)nbytes, voff, out);
     return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// ---- v_permlane32_swap probe: one wave swaps register a's upper 32 lanes with register b's
+// lower 32 lanes; in = a then b (64 words each), out = the two registers afterwards.
+namespace {
+
+__global__ void __launch_bounds__(64) probe_permlane32_swap_kernel(const uint32_t* in, uint32_t* out)
+{
+    const int l = (int)threadIdx.x;
+    const auto r = __builtin_amdgcn_permlane32_swap(in[l], in[64 + l], false, false);
+    out[l] = r[0];
+    out[64 + l] = r[1];
+}
+
+}  // namespace
+
+extern "C" int qpg_probe_permlane32_swap(const uint32_t* in, uint32_t* out, void* stream)
+{
+    if (!in || !out) return -1;
+    if (((uintptr_t)in | (uintptr_t)out) & 3) return -2;
+    if (!is_gfx950()) return -4;
+    hipLaunchKernelGGL(probe_permlane32_swap_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), in, out);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}

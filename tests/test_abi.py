@@ -228,7 +228,7 @@ def test_calib_library_exports_and_rejects():
     text = re.sub(r"/\*.*?\*/", "", open(CALIB_HEADER).read(), flags=re.S)
     names = re.findall(r"^\s*(?:int|int64_t)\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
     assert names == ["qpg_calib_mfma_i8", "qpg_calib_step", "qpg_calib_step_blocks", "qpg_probe_mfma",
-                     "qpg_probe_lds_dma"]
+                     "qpg_probe_lds_dma", "qpg_probe_permlane32_swap"]
     lib = ctypes.CDLL(CALIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -255,7 +255,13 @@ def test_calib_library_exports_and_rejects():
     assert dm(4, A16, 0, A16, A16, None) == EINVAL             # nbytes
     assert dm(4, None, 1024, A16, A16, None) == EINVAL
     assert dm(16, A8, 1024, A16, A16, None) == EALIGN          # src must be 16-byte aligned
+    ps = lib.qpg_probe_permlane32_swap
+    ps.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    ps.restype = ctypes.c_int
+    assert ps(None, A16, None) == EINVAL
+    assert ps(A16, ctypes.c_void_p((1 << 20) + 2), None) == EALIGN
     if not _has_gpu():
+        assert ps(A16, A16, None) == EDEVICE
         assert dm(16, A16, 1024, A16, A16, None) == EDEVICE
         assert st(2, 3, 100, A16, None) == EDEVICE
         assert pr(1, A8, A8, A16, A16, None) == EDEVICE     # 8-byte operands suffice for kind 1

@@ -14,6 +14,8 @@
   permutations, and offsets that are not multiples of 4 (the raw q6_K staging reads rows that
   start 2 bytes past a 4-byte boundary) -- and bytes past the descriptor's range read as zero
   (rows and tokens past the matrix).
+* v_permlane32_swap (the raw q6_K kernel's exchange of operand pieces between lane halves):
+  register a's lanes 32..63 trade places with register b's lanes 0..31.
 """
 import ctypes
 import os
@@ -178,3 +180,19 @@ def test_lds_direct_loads():
     for width, voff, nbytes in cases:
         got = run(width, voff, nbytes)
         assert np.array_equal(got, expect(width, voff, nbytes)), (width, voff[:3], nbytes)
+
+
+def test_permlane32_swap():
+    lib = ctypes.CDLL(CALIB)
+    f = lib.qpg_probe_permlane32_swap
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    a = np.arange(64, dtype=np.uint32) * 7 + 1000
+    b = np.arange(64, dtype=np.uint32) * 13 + 5000
+    inp = torch.from_numpy(np.concatenate([a, b]).view(np.int32)).to(DEV)
+    out = torch.zeros(128, dtype=torch.int32, device=DEV)
+    assert f(inp.data_ptr(), out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().view(np.uint32)
+    assert np.array_equal(o[:64], np.concatenate([a[:32], b[:32]]))
+    assert np.array_equal(o[64:], np.concatenate([a[32:], b[32:]]))
