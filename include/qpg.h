@@ -41,8 +41,9 @@
  *   q6_K weights: row-major, row j = K/256 consecutive 210-byte super-blocks:
  *       +0 ql[128] low 4 bits, +128 qh[64] high 2 bits, +192 int8 scales[16] (one per
  *       16 weights), +208 fp16 d. Weight = d*sc[e/16]*(q6 - 32). (GGUF q6_K.) Pointer
- *       must be 4-byte aligned; row starts inside the buffer are then only 2-byte aligned
- *       when K/256 is odd, which the kernel handles.
+ *       must be 2-byte aligned (the block's own alignment: its fp16 d). The MMQ kernels
+ *       stage the blocks by byte-addressed direct-to-LDS loads, so row and block starts
+ *       need no more; q6K_prepare alone asks for 4 bytes.
  *   q8_1 activations ("xq"), one buffer of qpg_q8_1_bytes(M, K) bytes, two planes:
  *       bytes [0, M*K):            int8 q[M][K], row-major
  *       bytes [M*K, M*K + 4*M*K/32): uint32 header[M][K/32]; low 16 bits = fp16 scale

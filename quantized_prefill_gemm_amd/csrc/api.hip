@@ -94,7 +94,7 @@ int mmq_checked(bool q6, const void* w, const void* xq, float* y, int32_t* s, in
     int rc = check_mmq_shape(M, N, K);
     if (rc != QPG_OK) return rc;
     if (s && M * N * (K / 16) >= ((int64_t)1 << 40)) return QPG_EINVAL;
-    if (!aligned(w, q6 ? 4 : 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4)))
+    if (!aligned(w, q6 ? 2 : 16) || !aligned(xq, 16) || (y && !aligned(y, 4)) || (s && !aligned(s, 4)))
         return QPG_EALIGN;
     rc = check_device();
     if (rc != QPG_OK) return rc;
@@ -191,7 +191,7 @@ int mmq_sk_checked(int form, const void* w, const void* xq, float* y, int64_t M,
         if (!ws || ws_bytes < (size_t)P * (size_t)M * (size_t)N * 4) return QPG_EINVAL;
         if (!aligned(ws, 16)) return QPG_EALIGN;
     }
-    const uintptr_t wa = form == 1 ? 4 : 16;
+    const uintptr_t wa = form == 1 ? 2 : 16;
     if (!aligned(w, wa) || !aligned(xq, 16) || !aligned(y, 4)) return QPG_EALIGN;
     const int rc = check_device();
     if (rc != QPG_OK) return rc;
@@ -357,7 +357,7 @@ static int mmq_f32(bool q6, const void* w, const float* x, float* y, int64_t M, 
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int rc = check_mmq_shape(M, N, K);
     if (rc != QPG_OK) return rc;
-    if (!aligned(x, 16) || !aligned(xq_ws, 16) || !aligned(w, q6 ? 4 : 16) || !aligned(y, 4)) return QPG_EALIGN;
+    if (!aligned(x, 16) || !aligned(xq_ws, 16) || !aligned(w, q6 ? 2 : 16) || !aligned(y, 4)) return QPG_EALIGN;
     rc = quantize_checked(x, xq_ws, M, K, s);
     if (rc != QPG_OK) return rc;
     return mmq_checked(q6, w, xq_ws, y, nullptr, M, N, K, s);

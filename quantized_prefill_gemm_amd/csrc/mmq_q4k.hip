@@ -18,9 +18,10 @@
 //    of raw qs) moved by LDS-direct buffer loads (buffer_load_dwordx4 ... lds): the loads
 //    of stage h+1 are issued before stage h is computed, land in LDS without passing
 //    through registers, and are waited for only at the next stage boundary. Each lane
-//    fetches the 16-byte granule that belongs at its LDS slot; rows are padded to an odd
-//    number of 16-byte slots (bank spread), pad slots are filled from an out-of-range
-//    offset (zeros), and so are tokens / rows past the end of the matrix. The block
+//    fetches the 16-byte granule that belongs at its LDS slot: rows are unpadded, and the
+//    source offsets permute the granules of a row so that LDS reads spread over the banks
+//    (layout below); tokens / rows past the end of the matrix read an out-of-range offset,
+//    which the buffer load returns as zeros. The block
 //    headers (q8_1 words, q4_K d/dmin/scales) are loaded into registers one super-block
 //    ahead and decoded once per super-block into per-(row, sub-block) and per-(token,
 //    chunk) f32 terms.

@@ -24,6 +24,7 @@ int main(int argc, char** argv)
     void* A16 = reinterpret_cast<void*>(1 << 20);           // never dereferenced
     void* A8 = reinterpret_cast<void*>((1 << 20) + 8);
     void* A2 = reinterpret_cast<void*>((1 << 20) + 2);
+    void* A1 = reinterpret_cast<void*>((1 << 20) + 1);
     float* F16 = static_cast<float*>(A16);
     float* F8 = static_cast<float*>(A8);
     for (int c = -6; c <= 1; ++c) CHECK(qpg_strerror(c) != nullptr);
@@ -36,7 +37,7 @@ int main(int argc, char** argv)
     CHECK(mmq_q4K(A16, F16, F16, 64, 256, 256, nullptr, nullptr) == QPG_EINVAL);
     CHECK(mmq_q6K(A16, F8, F16, 64, 256, 256, A16, nullptr) == QPG_EALIGN);
     CHECK(mmq_q4K_q8(A16, A16, F16, 0, 256, 256, nullptr) == QPG_EINVAL);
-    CHECK(mmq_q6K_q8(A2, A16, F16, 64, 256, 256, nullptr) == QPG_EALIGN);
+    CHECK(mmq_q6K_q8(A1, A16, F16, 64, 256, 256, nullptr) == QPG_EALIGN);
     CHECK(mmq_q4K_isums(A16, A16, nullptr, 64, 256, 256, nullptr) == QPG_EINVAL);
     CHECK(mmq_q6K_isums(A16, A16, static_cast<int32_t*>(A16), 64, 256, 288, nullptr) == QPG_EINVAL);
     CHECK(q6K_prepare(A2, A16, 128, 256, nullptr) == QPG_EALIGN);
@@ -60,6 +61,7 @@ int main(int argc, char** argv)
     if (nodevice) {
         CHECK(quantize_q8_1(F16, A16, 64, 256, nullptr) == QPG_EDEVICE);
         CHECK(mmq_q4K_q8(A16, A16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);
+        CHECK(mmq_q6K_q8(A2, A16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);   // 2-byte q6_K blocks
         CHECK(mmq_q4K_noalloc(A16, F16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);
         CHECK(mmq_q6K_exp_q8_sk(A16, A16, F16, 64, 256, 4096, A16, 5u * 64u * 256u * 4u, nullptr) == QPG_EDEVICE);
         CHECK(qpg_calib_step_blocks(3) == 0);

@@ -82,6 +82,7 @@ def test_strerror_and_sizes(L):
 
 
 A16 = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: every call below fails validation
+A1 = ctypes.c_void_p((1 << 20) + 1)
 A2 = ctypes.c_void_p((1 << 20) + 2)
 A8 = ctypes.c_void_p((1 << 20) + 8)
 
@@ -118,9 +119,11 @@ def test_mmq_q8_rejects(L, fn, args, expect):
 
 
 def test_alignment_rules_per_type(L):
-    # q4_K weights need 16-byte alignment, q6_K weights 4-byte
+    # q4_K weights need 16-byte alignment, raw q6_K weights 2-byte (the block's fp16 d)
     assert L.mmq_q4K_q8(A8, A16, A16, 64, 256, 256, None) == EALIGN
-    assert L.mmq_q6K_q8(A2, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K_q8(A1, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K_isums(A1, A16, A16, 64, 256, 256, None) == EALIGN
+    assert L.mmq_q6K(A1, A16, A16, 64, 256, 256, A16, None) == EALIGN
     assert L.mmq_q4K(A16, A8, A16, 64, 256, 256, A16, None) == EALIGN     # x
     assert L.mmq_q4K(A16, A16, A16, 64, 256, 256, A8, None) == EALIGN     # workspace
     assert L.mmq_q6K(A16, A16, A16, 64, 256, 256, None, None) == EINVAL   # missing workspace
@@ -189,7 +192,7 @@ def test_splitk_rejects(L):
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A16, need - 4, None) == EINVAL  # too small
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 512, 512, 4096, A8, need, None) == EALIGN
     assert L.mmq_q4K_q8_sk(A8, A16, A16, 512, 512, 4096, A16, need, None) == EALIGN
-    assert L.mmq_q6K_q8_sk(A2, A16, A16, 512, 512, 4096, A16, need6, None) == EALIGN      # q6_K: 4 bytes
+    assert L.mmq_q6K_q8_sk(A1, A16, A16, 512, 512, 4096, A16, need6, None) == EALIGN      # q6_K: 2 bytes
     assert L.mmq_q6K_prep_q8_sk(A16, A16, A16, 512, 512, 1 << 24, A16, need, None) == EINVAL
     assert L.mmq_q6K_exp_q8_sk(None, A16, A16, 512, 512, 4096, A16, need, None) == EINVAL
     assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 512, 512, 288, A16, need, None) == EINVAL
@@ -212,6 +215,8 @@ def test_valid_call_without_device_reports_edevice(L):
     assert L.q6K_prepare(A16, A16, 128, 256, None) == EDEVICE
     assert L.mmq_q6K_prep_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
     assert L.q6K_expand(A2, A16, 64, 256, None) == EDEVICE          # raw blocks: any alignment
+    assert L.mmq_q6K_q8(A2, A16, A16, 64, 256, 256, None) == EDEVICE  # raw q6_K MMQ: 2-byte blocks
+    assert L.mmq_q6K(A2, A16, A16, 64, 256, 256, A16, None) == EDEVICE
     assert L.mmq_q6K_exp_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
     # no split for this shape: the workspace may be absent
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 64, 256, 1280, None, 0, None) == EDEVICE

@@ -160,6 +160,44 @@ def test_mmq_tails(wtype, M, N, K):
     check_out(gpu_mmq(wtype, W, X, N), O.mmq(wtype, W, X), f"{wtype} {M}x{N}x{K}")
 
 
+def dev_at(a: np.ndarray, shift: int) -> torch.Tensor:
+    """The bytes of a on the device, starting `shift` bytes past a 256-byte boundary (a view
+    into a larger buffer)."""
+    b = np.ascontiguousarray(a).reshape(-1).view(np.uint8)
+    buf = torch.zeros(b.size + 256, dtype=torch.uint8, device=DEV)
+    v = buf[shift:shift + b.size]
+    v.copy_(torch.from_numpy(b))
+    return v
+
+
+@pytest.mark.parametrize("shift", [2, 6])
+@pytest.mark.parametrize("M,N,K", [(33, 130, 768), (100, 200, 1024), (65, 257, 2816), (512, 130, 11008)])
+def test_q6K_raw_blocks_at_two_byte_alignment(M, N, K, shift):
+    """Raw q6_K blocks at an address that is 2 mod 4 (the blocks' own alignment, their fp16 d):
+    integer sums bit-exact against the oracle, outputs within the tolerance, through the q8,
+    f32 and K-split entry points; every row start is then 2 mod 4 (K/256 even) or alternates
+    (K/256 odd)."""
+    say(f"[q6_K raw blocks at +{shift}: {M}x{N}x{K}]")
+    W, X = inputs.small_case("q6_K", M, N, K, seed=21 + shift, gain=True)
+    w = dev_at(W, shift)
+    assert w.data_ptr() % 4 == 2
+    xq, (q, _, _) = gpu_quantize(X)
+    s = B.mmq_q6K_isums(w, xq, M, N, K)
+    y = B.mmq_q6K_q8(w, xq, M, N, K)
+    yf = B.mmq_q6K(w, dev(X), N)
+    ysk = B.mmq_q6K_q8_sk(w, xq, M, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy(), O.isums("q6_K", W, q))
+    r = O.mmq("q6_K", W, X)
+    check_out(y.cpu().numpy(), r, f"q8 entry +{shift}")
+    assert torch.equal(yf, y)
+    check_out(ysk.cpu().numpy(), r, f"split-K entry +{shift}")
+    # the same blocks 16-byte aligned give the same outputs bit for bit
+    y16 = B.mmq_q6K_q8(dev(W.reshape(-1)), xq, M, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y)
+
+
 @pytest.mark.parametrize("wtype", ["q4_K", "q6_K"])
 def test_f32_entry_equals_quantize_then_q8(wtype):
     M, N, K = 96, 200, 1024
