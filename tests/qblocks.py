@@ -93,3 +93,25 @@ def tolerance_ok(g: np.ndarray, r: np.ndarray, rel=1e-4, abs_unit=1e-3):
     big = np.abs(r) >= s
     relmax = float(np.max(err[big] / np.abs(r[big]))) if np.any(big) else 0.0
     return ratio <= 1.0, ratio, relmax
+
+
+def near_tie_blocks(amax: float) -> np.ndarray:
+    """32-value blocks whose first value is amax = 127 * 2^-t (so d = 2^-t and 1/d = 2^t are
+    exact and x * (1/d) is exact too) and whose other 31 values put x * (1/d) at n + 1/2 and
+    up to three f32 steps either side of it, for n = 0..126 and both signs: every rounding
+    decision of the int8 conversion next to a tie."""
+    s = amax / 127.0
+    v = []
+    for n in range(127):
+        t = np.float32(n + 0.5)
+        for k in range(-3, 4):
+            c = t
+            for _ in range(abs(k)):
+                c = np.nextafter(c, np.float32(np.inf if k > 0 else -np.inf), dtype=np.float32)
+            if c <= 127.0:
+                v += [c, -c]
+    v = np.array(v, np.float32) * np.float32(s)
+    v = np.concatenate([v, np.zeros((-len(v)) % 31, np.float32)]).reshape(-1, 31)
+    blocks = np.concatenate([np.full((len(v), 1), amax, np.float32), v], axis=1)
+    blocks = np.concatenate([blocks, np.zeros(((-len(blocks)) % 8, 32), np.float32)])
+    return blocks.reshape(-1, 256)

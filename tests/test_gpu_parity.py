@@ -17,7 +17,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 from oracle import oracle as O
-from qblocks import tolerance_ok, encode_q4K, encode_q6K
+from qblocks import tolerance_ok, encode_q4K, encode_q6K, near_tie_blocks
 from quantized_prefill_gemm_amd import binding as B
 from quantized_prefill_gemm_amd import inputs
 
@@ -85,6 +85,16 @@ def test_quantize_edge_cases():
     }
     for tag, x in cases.items():
         assert_q8_equal(x, tag)
+
+
+@pytest.mark.parametrize("amax", [127.0, 63.5, 127.0 * 2.0 ** -20])
+def test_quantize_near_ties(amax):
+    say(f"[quantize near ties, amax {amax}]")
+    x = near_tie_blocks(amax)
+    b = x.reshape(-1, 32)
+    live = np.any(b != 0, axis=1)                    # the rest are zero blocks filling the rows
+    assert (b[live, 0] == np.float32(amax)).all() and live.sum() == 58
+    assert_q8_equal(x, f"near ties, amax {amax}")
 
 
 # ----------------------------------------------------------------------------- integer stage

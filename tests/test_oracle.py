@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import oracle as O
-from qblocks import encode_q4K, encode_q6K, f16_bits
+from qblocks import encode_q4K, encode_q6K, f16_bits, near_tie_blocks
 from quantized_prefill_gemm_amd import inputs
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -94,6 +94,27 @@ def test_q8_1_ramp_exact_rationals():
         assert int(ss[0, 0]) == sum(exp)
         d = np.float32(np.float32(31 * scale) / np.float32(127))   # IEEE f32 division (numpy)
         assert int(dh[0, 0]) == int(np.array(d, np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("amax", [127.0, 63.5, 127.0 * 2.0 ** -20])
+def test_q8_1_near_ties_exact(amax):
+    """Blocks whose scale d = amax/127 is a power of two, so x * (1/d) is exact and q must be
+    the exact rational x/d rounded half away from zero: values at n + 1/2 and up to three f32
+    steps either side, n = 0..126, both signs (the quantiser's rounding reading)."""
+    x = near_tie_blocks(amax)
+    q, dh, ss = O.quantize_q8_1(x)
+    d = Fraction(amax) / 127
+    flat = x.reshape(-1)
+    exp = np.empty(flat.size, np.int64)
+    for i, v in enumerate(flat.tolist()):
+        r = abs(Fraction(v) / d)
+        n = r.numerator // r.denominator
+        n += 1 if r - n >= Fraction(1, 2) else 0
+        exp[i] = n if v >= 0 else -n
+    assert np.array_equal(q.reshape(-1).astype(np.int64), exp)
+    blocks = exp.reshape(-1, 32)
+    assert np.array_equal(ss.reshape(-1).astype(np.int64), blocks.sum(axis=1))
+    assert np.count_nonzero(np.abs(blocks[:, 1:]) >= 1) > 1500
 
 
 def test_q8_1_negation_and_bounds():
