@@ -23,9 +23,11 @@
 //    and the raw weight bytes by 16-byte loads straight from the blocks. A lane's source
 //    offset may be any byte offset (rows of 210-byte blocks start only 2-byte aligned when
 //    K/256 is odd), so rows need no register staging and no shifts; the per-lane offsets
-//    apply the row swizzle. Each wave loads exactly its own 32 weight rows (and their int8
-//    scales and d), so after its own load wait it converts their d*sc for the stage without
-//    another barrier; the barrier is for the q8 tile and header words, which every wave reads.
+//    apply the row swizzle. Each wave loads exactly its own 32 weight rows, and with the first
+//    stage of a super-block their 16 int8 scales and d (one 16-byte and one dword load of 32
+//    lanes, a row each: rows are far apart, so a load costs by the rows it touches), so after
+//    its own load wait it converts their d*sc for both stages without another barrier; the
+//    barrier is for the q8 tile and header words, which every wave reads.
 //  * LDS: rows of the ql and qh halves XOR-swizzled in 16-byte granules (reads of 16
 //    consecutive rows hit 16 bank groups). A K=16 MFMA wants k-group l>>5 of its sub-block in
 //    lane l: 8 bytes of each of the chunk's two sub-blocks. The prepared form (q6K_prepare:
@@ -62,15 +64,15 @@ struct StageLds {
     alignas(16) uint8_t bh[TN * 32];
     alignas(16) float dsc[8][TN];       // d*sc per sub-block of the stage, rows in C-register order per wave
     alignas(16) uint32_t hw[4][TM];     // q8_1 header words (fp16 da | ssum) per chunk of the stage and token
-    // raw blocks: each wave's 32 rows, the stage's 8 int8 scales (2 words per row) and the word
-    // holding fp16 d (block bytes 206..209: d in the high half), as loaded
-    alignas(16) uint32_t wsc[4][64];
-    alignas(16) uint32_t wd[4][32];
 };
 struct GroupLds {
     StageLds st[2];
+    // raw blocks, per wave and super-block, as loaded: the 16 int8 scales of each of the wave's
+    // 32 rows (4 words per row), then the word holding fp16 d (block bytes 206..209, d in the
+    // high half) of each row
+    alignas(16) uint32_t wsd[4][32 * 4 + 32];
 };
-static_assert(sizeof(GroupLds) == 54272, "LDS of one group");
+static_assert(sizeof(GroupLds) == 53760, "LDS of one group");
 static_assert(3 * sizeof(GroupLds) <= 160 * 1024, "three groups per CU");
 static_assert(sizeof(GroupLds) >= TM * TN * 4, "a group's buffers hold its partial tile");
 
@@ -178,7 +180,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
     // stage half; qh: row sl >> 1, granule (sl & 1) ^ bh_sw(row). A slab is 64 slots (1 KiB);
     // wave w loads ql slabs 2w, 2w + 1 and qh slab w, i.e. exactly its own 32 rows, and the
     // scales and d of those rows.
-    unsigned voL[2], voB = 0, voS = 0, voD = 0;
+    unsigned voL[2], voB = 0, voS = 0;
     if constexpr (!PREP) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -191,8 +193,7 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
             const int j = sl >> 1;
             voB = (unsigned)(j * wrow + 16 * ((sl & 1) ^ bh_sw(j)));
         }
-        voS = (unsigned)((32 * wave + (lane >> 1)) * wrow + 4 * (lane & 1));
-        voD = (unsigned)((32 * wave + (lane & 31)) * wrow);
+        voS = (unsigned)((32 * wave + (lane & 31)) * wrow);     // lanes 0..31: row 32 wave + lane
     }
     const uint8_t* const wbase = W + (size_t)n0 * wrow;
     const unsigned nW = (unsigned)(rows_w * wrow);
@@ -217,9 +218,11 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
 #pragma unroll
             for (int i = 0; i < 2; ++i) lds_load16(rL, st.bl + 1024 * (2 * wave + i), (int)voL[i]);
             lds_load16(rB, st.bh + 1024 * wave, (int)voB);
-            if constexpr (!ISUMS) {
-                lds_load4(wdesc(blk + 192 + 8 * hh), &st.wsc[wave][0], (int)voS);
-                if (lane < 32) lds_load4(wdesc(blk + 206), &st.wd[wave][0], (int)voD);
+            // the scales and d of the super-block, once (with its first stage): 32 lanes, one row
+            // each, 16 bytes of scales and the word holding d
+            if (!ISUMS && hh == 0 && lane < 32) {
+                lds_load16(wdesc(blk + 192), &G.wsd[wave][0], (int)voS);
+                lds_load4(wdesc(blk + 206), &G.wsd[wave][128], (int)voS);
             }
         }
         if constexpr (!ISUMS) lds_load4(rH, &st.hw[wave][0], voH + (sb * 8 + 4 * hh) * 4);
@@ -236,16 +239,20 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
     const int wr = 32 * wave + l32;                  // weight row of this lane's A operand
     const int tsw = aq_sw(l32);                      // tokens l32 and l32 + 32 share the swizzle
 
-    // d*sc of this wave's 32 rows for the stage's 8 sub-blocks, from the scale words and d the
-    // wave loaded itself (so only its own load wait is needed): lane (jj, half) converts the
-    // four scales 4 half .. 4 half + 3 of row 32 wave + jj.
-    auto decode_dsc = [&](StageLds& st) {
+    // d*sc of this wave's 32 rows for all 16 sub-blocks of the super-block, from the scales and
+    // d the wave loaded itself (so only its own load wait is needed), at its first stage: lane
+    // (jj, half) converts the eight scales of stage `half` of row 32 wave + jj into that stage's
+    // buffer (the other buffer's d*sc was last read by this wave's own previous stage).
+    auto decode_dsc = [&]() {
         const int jj = l32;
-        const uint32_t scw = st.wsc[wave][2 * jj + hg];
-        const float d = half_bits_to_float(st.wd[wave][jj] >> 16);
+        const uint32_t* sw = &G.wsd[wave][4 * jj + 2 * hg];
+        const uint32_t s0 = sw[0], s1 = sw[1];
+        const float d = half_bits_to_float(G.wsd[wave][128 + jj] >> 16);
         const int pos = 32 * wave + c_pos(jj);
+        StageLds& st = G.st[hg];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st.dsc[4 * hg + e][pos] = d * (float)(int)(int8_t)(scw >> (8 * e));   // exact
+        for (int e = 0; e < 8; ++e)
+            st.dsc[e][pos] = d * (float)(int)(int8_t)((e < 4 ? s0 : s1) >> (8 * (e & 3)));   // exact
     };
 
     // Integer stage + fold over the four chunks of one stage (chunk cl = sub-blocks 2cl and
@@ -342,7 +349,8 @@ __global__ void __launch_bounds__(256 * KS, KS > 1 ? 1 : 3) mmq_q6K_kernel(
         __syncthreads();                    // stage h visible in buffer cur; buffer cur^1 free
         if (h + 1 < nst) issue_stage(sb0 + ((h + 1) >> 1), (h + 1) & 1, G.st[cur ^ 1]);
         if (h < nst) {
-            if constexpr (!PREP && !ISUMS) decode_dsc(G.st[cur]);
+            if constexpr (!PREP && !ISUMS)
+                if (hh == 0) decode_dsc();
             compute_stage(sb, hh, G.st[cur]);
         }
     }
