@@ -227,7 +227,8 @@ def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
             "kernel": "v_mfma_i32_32x32x32_i8 chains, 2 waves per SIMD", "seconds": round(secs, 5)}
 
 
-STEP_MODES = {0: "mfma_only", 1: "fold_only", 2: "kernel_step", 3: "mfma_and_independent_fold"}
+STEP_MODES = {0: "mfma_only", 1: "fold_only", 2: "kernel_step", 3: "mfma_and_independent_fold",
+              4: "mfma_then_own_fold"}
 
 
 def measured_step_ceiling(waves=(2, 3, 4), iters: int = 4000):

@@ -12,7 +12,9 @@
 //   mode 1  the fold alone (its F operands made opaque per step instead of MFMA results),
 //   mode 2  the kernel's step: MFMA one step ahead, fold of the previous result,
 //   mode 3  MFMA and fold with no dependency between them (the fold reads opaque values):
-//           shows whether the matrix core and the VALU run concurrently at all.
+//           shows whether the matrix core and the VALU run concurrently at all,
+//   mode 4  each step's MFMA folded in the same step (no look-ahead: half the result
+//           registers; other waves on the SIMD have to cover the MFMA's latency).
 // Occupancy is fixed by the launch: 256 * W workgroups of four waves, each holding
 // 160 KiB / W of LDS (touched once), so every CU runs exactly W workgroups and each SIMD
 // W waves.
@@ -65,19 +67,21 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
 
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
-    if constexpr (MODE != 1) F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
+    if constexpr (MODE != 1 && MODE != 4) F[0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             asm volatile("" : "+v"(magic));
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (MODE != 1) {
+            if constexpr (MODE == 4) {
+                F[k & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
+            } else if constexpr (MODE != 1) {
                 F[(k + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
                 if constexpr (MODE == 0 || MODE == 3) asm volatile("" : : "v"(F[(k + 1) & 1]));
             }
             if constexpr (MODE != 0) {
                 int32x16 Fk;
-                if constexpr (MODE == 2) {
+                if constexpr (MODE == 2 || MODE == 4) {
                     Fk = F[k & 1];
                 } else {
                     asm volatile("" : "+v"(opaque));       // a new, unknown value every step
@@ -144,7 +148,7 @@ extern "C" int64_t qpg_calib_step_blocks(int waves_per_simd)
 
 extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream)
 {
-    if (!out || mode < 0 || mode > 3 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
+    if (!out || mode < 0 || mode > 4 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
         return -1;
     if (((uintptr_t)out & 7) != 0) return -2;
     int cus = 0;
@@ -157,7 +161,8 @@ extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint6
     case 0: e = launch_mode<0>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 1: e = launch_mode<1>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 2: e = launch_mode<2>(waves_per_simd, blocks, (int)iters, out, s); break;
-    default: e = launch_mode<3>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 3: e = launch_mode<3>(waves_per_simd, blocks, (int)iters, out, s); break;
+    default: e = launch_mode<4>(waves_per_simd, blocks, (int)iters, out, s); break;
     }
     return e == hipSuccess ? 0 : -3;
 }
