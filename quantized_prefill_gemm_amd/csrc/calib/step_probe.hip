@@ -14,7 +14,12 @@
 //   mode 3  MFMA and fold with no dependency between them (the fold reads opaque values):
 //           shows whether the matrix core and the VALU run concurrently at all,
 //   mode 4  each step's MFMA folded in the same step (no look-ahead: half the result
-//           registers; other waves on the SIMD have to cover the MFMA's latency).
+//           registers; other waves on the SIMD have to cover the MFMA's latency),
+//   mode 5  the kernel's step with its operands read from LDS as the kernel reads them: per
+//           step the 16-byte B operand and the (da, -1.5*2^23*da) pair, every second step
+//           the 16-byte raw weight word (unpacked to nibbles) and the 16 d*sc values,
+//   mode 6  mode 5 with every LDS operand read one step before the step that uses it
+//           (double-buffered in registers), so no read is waited for in its own step.
 // Occupancy is fixed by the launch: 256 * W workgroups of four waves, each holding
 // 160 KiB / W of LDS (touched once), so every CU runs exactly W workgroups and each SIMD
 // W waves.
@@ -43,7 +48,9 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
 {
     __shared__ int cap[LdsCap<W>::bytes / 4];
     const int tx = (int)threadIdx.x, lane = tx & 63;
-    cap[tx] = tx;
+    // operand area of mode 5 (16 KiB): small finite floats, any bytes for the int8 operands
+    for (int i = tx; i < 4096; i += 256) cap[i] = __float_as_int(0.0009765625f * (float)(1 + (i & 7)));
+    __syncthreads();
     int32x4 a = {lane * 0x01010101, 0x0F0E0D0C, 0x07060504 ^ lane, (int)blockIdx.x};
     const int32x4 b = {0x7F017F01, tx * 3, 0x10203040, -tx};
     int32x16 magic;
@@ -51,9 +58,17 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
     for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
     // fold terms: da is an exact f16 value, c0 = -1.5*2^23*da exact, dsv per register
     const float da = 0.0078125f * (float)(1 + (lane & 7)), c0 = -kMagic * da;
+    float dal = da, c0l = c0;       // modes 5 and 6 read them from LDS every step
     float dsv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) dsv[r] = 0.001f * (float)(r + 1 + (lane & 3));
+    // mode 6: operands read one step ahead, double-buffered
+    int32x4 ab[2] = {a, a}, bb[2] = {b, b};
+    float dsb[2][16];
+    int2 adb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dsb[0][r] = dsb[1][r] = dsv[r];
+    adb[0] = adb[1] = int2{__float_as_int(da), __float_as_int(c0)};
     floatx16 y[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -73,7 +88,55 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
         for (int k = 0; k < 8; ++k) {
             asm volatile("" : "+v"(magic));
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (MODE == 4) {
+            if constexpr (MODE == 6) {
+                // this step: MFMA k+1 with the B operand read last step, fold k with the d*sc and
+                // (da, c0) read last step; then the reads for step k+1 (B of MFMA k+2)
+                __builtin_amdgcn_sched_barrier(0);
+                F[(k + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ab[k & 1], bb[k & 1], magic, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dsv[r] = dsb[k & 1][r];
+                dal = __int_as_float(adb[k & 1].x);
+                c0l = __int_as_float(adb[k & 1].y);
+                const int kn = k + 1;
+                bb[kn & 1] = *reinterpret_cast<const int32x4*>(&cap[((kn & 3) * 1024 + lane * 16) / 4]);
+                if ((kn & 1) == 0)
+                    ab[kn & 1] = *reinterpret_cast<const int32x4*>(&cap[(4096 + (kn & 2) * 512 + lane * 16) / 4]) & 0x0F0F0F0F;
+                else
+                    ab[kn & 1] = ab[k & 1];
+                if ((kn & 1) == 0) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int32x4 d4 = *reinterpret_cast<const int32x4*>(&cap[(8192 + ((kn >> 1) & 3) * 512 + (lane >> 5) * 64 + q4 * 16) / 4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dsb[kn & 1][4 * q4 + e] = __int_as_float(d4[e]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dsb[kn & 1][r] = dsb[k & 1][r];
+                }
+                adb[kn & 1] = *reinterpret_cast<const int2*>(&cap[(12288 + (kn & 7) * 256 + (lane & 31) * 8) / 4]);
+            } else if constexpr (MODE == 5) {
+                // operands of this step from LDS: B of the next MFMA, raw weights every other
+                // step, then this fold's d*sc (every other step) and (da, c0)
+                const int32x4 bn = *reinterpret_cast<const int32x4*>(&cap[((k & 3) * 1024 + lane * 16) / 4]);
+                if ((k & 1) == 0) {
+                    const int32x4 raw = *reinterpret_cast<const int32x4*>(&cap[(4096 + (k & 2) * 512 + lane * 16) / 4]);
+                    a = raw & 0x0F0F0F0F;
+                }
+                if ((k & 1) == 0) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int32x4 d4 = *reinterpret_cast<const int32x4*>(&cap[(8192 + ((k >> 1) & 3) * 512 + (lane >> 5) * 64 + q4 * 16) / 4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) dsv[4 * q4 + e] = __int_as_float(d4[e]);
+                    }
+                }
+                const int2 ad = *reinterpret_cast<const int2*>(&cap[(12288 + (k & 7) * 256 + (lane & 31) * 8) / 4]);
+                dal = __int_as_float(ad.x);
+                c0l = __int_as_float(ad.y);
+                __builtin_amdgcn_sched_barrier(0);
+                F[(k + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bn, magic, 0, 0, 0);
+            } else if constexpr (MODE == 4) {
                 F[k & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
             } else if constexpr (MODE != 1) {
                 F[(k + 1) & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, magic, 0, 0, 0);
@@ -81,7 +144,7 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
             }
             if constexpr (MODE != 0) {
                 int32x16 Fk;
-                if constexpr (MODE == 2 || MODE == 4) {
+                if constexpr (MODE == 2 || MODE >= 4) {
                     Fk = F[k & 1];
                 } else {
                     asm volatile("" : "+v"(opaque));       // a new, unknown value every step
@@ -89,7 +152,7 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float e = fmaf(__int_as_float(Fk[r]), da, c0);
+                    const float e = fmaf(__int_as_float(Fk[r]), dal, c0l);
                     y[k & 1][r] = fmaf(e, dsv[r], y[k & 1][r]);
                 }
             }
@@ -148,7 +211,7 @@ extern "C" int64_t qpg_calib_step_blocks(int waves_per_simd)
 
 extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream)
 {
-    if (!out || mode < 0 || mode > 4 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
+    if (!out || mode < 0 || mode > 6 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
         return -1;
     if (((uintptr_t)out & 7) != 0) return -2;
     int cus = 0;
@@ -162,7 +225,9 @@ extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint6
     case 1: e = launch_mode<1>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 2: e = launch_mode<2>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 3: e = launch_mode<3>(waves_per_simd, blocks, (int)iters, out, s); break;
-    default: e = launch_mode<4>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 4: e = launch_mode<4>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 5: e = launch_mode<5>(waves_per_simd, blocks, (int)iters, out, s); break;
+    default: e = launch_mode<6>(waves_per_simd, blocks, (int)iters, out, s); break;
     }
     return e == hipSuccess ? 0 : -3;
 }
