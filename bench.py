@@ -12,6 +12,8 @@ Other modes:
   --shards                   the N/8 shares of the 7B layer GEMMs, plain vs K-split entry
                              points (one JSON line per shape)
   --msweep                   the 7B layer GEMM shapes at M = 16 .. 2048 tokens, likewise
+  --q6forms                  the raw, prepared and expanded q6_K forms on the v and down
+                             shapes at M = 16 .. 1024, likewise
 For rocprofv3 runs:
   --profile {q4K,q6K,q6Kp,q6Kx,quant}  a few launches of one kernel (q6_K raw / prepared /
                              expanded), no timing output
@@ -384,6 +386,9 @@ MSWEEP_M = (16, 64, 128, 256, 512, 1024, 2048)
 MSWEEP_SHAPES = [("q4K", 4096, 4096, "q/k/o 4096x4096 q4_K"), ("q6K_exp", 4096, 4096, "v 4096x4096 q6_K expanded"),
                  ("q4K", 11008, 4096, "gate/up 11008x4096 q4_K"), ("q6K_exp", 4096, 11008, "down 4096x11008 q6_K expanded")]
 
+Q6FORMS_M = (16, 64, 128, 256, 512, 1024)
+Q6FORMS_SHAPES = [(4096, 4096, "v 4096x4096"), (4096, 11008, "down 4096x11008")]
+
 SHARD_SHAPES = [("q4K", 512, 1376, 4096, "gate/up share"), ("q4K", 512, 512, 4096, "q/k/v/o share"),
                 ("q6K", 512, 512, 11008, "down share, raw q6_K"), ("q6K_prep", 512, 512, 11008, "down share, prepared"),
                 ("q6K_exp", 512, 512, 11008, "down share, expanded"), ("q4K", 128, 4096, 4096, "short prompt")]
@@ -475,6 +480,8 @@ def main():
                     help="time the N/8 shares of the 7B layer GEMMs: plain vs K-split entry points")
     ap.add_argument("--msweep", action="store_true",
                     help="time the 7B layer GEMM shapes over M = 16..2048 tokens: plain vs K-split entry points")
+    ap.add_argument("--q6forms", action="store_true",
+                    help="time the three q6_K weight forms on the v and down shapes over M = 16..1024")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}): this build has no multi-GPU path; "
@@ -486,9 +493,14 @@ def main():
     if a.profile:
         profile_mode(a.profile, a.launches)
         return
-    if a.shards or a.msweep:
-        shapes = None if a.shards else [(f, m, n, k, f"{what}, M={m}") for f, n, k, what in MSWEEP_SHAPES
-                                        for m in MSWEEP_M]
+    if a.shards or a.msweep or a.q6forms:
+        if a.shards:
+            shapes = None
+        elif a.msweep:
+            shapes = [(f, m, n, k, f"{what}, M={m}") for f, n, k, what in MSWEEP_SHAPES for m in MSWEEP_M]
+        else:
+            shapes = [(f, m, n, k, f"{what} {f} M={m}") for n, k, what in Q6FORMS_SHAPES for m in Q6FORMS_M
+                      for f in ("q6K", "q6K_prep", "q6K_exp")]
         run_shards(a.steps if a.steps != ap.get_default("steps") else (300 if a.shards else 100),
                    a.warmup if a.warmup != ap.get_default("warmup") else (100 if a.shards else 30), shapes)
         return
