@@ -231,7 +231,7 @@ def measured_mfma_peak(iters: int = 20000, blocks: int = 512):
 
 STEP_MODES = {0: "mfma_only", 1: "fold_only", 2: "kernel_step", 3: "mfma_and_independent_fold",
               4: "mfma_then_own_fold", 5: "kernel_step_operands_from_lds",
-              6: "kernel_step_operands_from_lds_one_step_ahead"}
+              6: "kernel_step_operands_from_lds_one_step_ahead", 7: "kernel_step_fold_in_groups_of_4"}
 
 
 def measured_step_ceiling(waves=(2, 3, 4), iters: int = 4000):

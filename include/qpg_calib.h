@@ -36,7 +36,8 @@ int qpg_calib_mfma_i8(int64_t blocks, int64_t iters, uint64_t* out, void* stream
  *   3: MFMAs and a fold that does not depend on them (do the two units run concurrently);
  *   4: each MFMA folded in its own step (no look-ahead); 5: the kernel's step with its
  *   operands (B, raw weights, d*sc, da pair) read from LDS as the kernel reads them;
- *   6: mode 5 with every LDS operand read one step ahead (double-buffered in registers).
+ *   6: mode 5 with every LDS operand read one step ahead (double-buffered in registers);
+ *   7: the kernel's step with its fold issued in groups of four independent FMAs.
  * waves_per_simd in {2, 3, 4}: the launch holds exactly that many waves on every SIMD
  * (qpg_calib_step_blocks(w) workgroups of four waves, LDS sized so that w fit a CU).
  * Every wave runs iters x 8 steps. out: device pointer to qpg_calib_step_blocks(w) * 4

@@ -19,7 +19,9 @@
 //           step the 16-byte B operand and the (da, -1.5*2^23*da) pair, every second step
 //           the 16-byte raw weight word (unpacked to nibbles) and the 16 d*sc values,
 //   mode 6  mode 5 with every LDS operand read one step before the step that uses it
-//           (double-buffered in registers), so no read is waited for in its own step.
+//           (double-buffered in registers), so no read is waited for in its own step,
+//   mode 7  the kernel's step (as mode 2) with the fold issued in groups of four: four
+//           independent first FMAs, then the four accumulating ones.
 // Occupancy is fixed by the launch: 256 * W workgroups of four waves, each holding
 // 160 KiB / W of LDS (touched once), so every CU runs exactly W workgroups and each SIMD
 // W waves.
@@ -150,10 +152,24 @@ __global__ void __launch_bounds__(256, W) step_kernel(int iters, uint64_t* out)
                     asm volatile("" : "+v"(opaque));       // a new, unknown value every step
                     Fk = opaque;
                 }
+                if constexpr (MODE == 7) {
+                    // the fold in groups of four: four independent first FMAs, then the four
+                    // accumulating ones (no FMA waits on the one just before it)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = fmaf(__int_as_float(Fk[r]), dal, c0l);
-                    y[k & 1][r] = fmaf(e, dsv[r], y[k & 1][r]);
+                    for (int g = 0; g < 4; ++g) {
+                        float e[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) e[j] = fmaf(__int_as_float(Fk[4 * g + j]), dal, c0l);
+                        asm volatile("" : "+v"(e[0]), "+v"(e[1]), "+v"(e[2]), "+v"(e[3]));
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) y[k & 1][4 * g + j] = fmaf(e[j], dsv[4 * g + j], y[k & 1][4 * g + j]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float e = fmaf(__int_as_float(Fk[r]), dal, c0l);
+                        y[k & 1][r] = fmaf(e, dsv[r], y[k & 1][r]);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -211,7 +227,7 @@ extern "C" int64_t qpg_calib_step_blocks(int waves_per_simd)
 
 extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream)
 {
-    if (!out || mode < 0 || mode > 6 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
+    if (!out || mode < 0 || mode > 7 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
         return -1;
     if (((uintptr_t)out & 7) != 0) return -2;
     int cus = 0;
@@ -227,7 +243,8 @@ extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint6
     case 3: e = launch_mode<3>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 4: e = launch_mode<4>(waves_per_simd, blocks, (int)iters, out, s); break;
     case 5: e = launch_mode<5>(waves_per_simd, blocks, (int)iters, out, s); break;
-    default: e = launch_mode<6>(waves_per_simd, blocks, (int)iters, out, s); break;
+    case 6: e = launch_mode<6>(waves_per_simd, blocks, (int)iters, out, s); break;
+    default: e = launch_mode<7>(waves_per_simd, blocks, (int)iters, out, s); break;
     }
     return e == hipSuccess ? 0 : -3;
 }

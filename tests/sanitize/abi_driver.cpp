@@ -55,7 +55,7 @@ int main(int argc, char** argv)
     CHECK(mmq_q4K_noalloc(A16, F16, F16, 2711, 256, 11008, nullptr) == QPG_ESCRATCH);
     CHECK(mmq_q4K_noalloc(A8, F16, F16, 64, 256, 256, nullptr) == QPG_EALIGN);
     CHECK(qpg_calib_mfma_i8(0, 10, static_cast<uint64_t*>(A16), nullptr) == -1);
-    CHECK(qpg_calib_step(7, 3, 10, static_cast<uint64_t*>(A16), nullptr) == -1);
+    CHECK(qpg_calib_step(8, 3, 10, static_cast<uint64_t*>(A16), nullptr) == -1);
     CHECK(qpg_probe_mfma(0, A8, A16, A16, A16, nullptr) == -2);
     CHECK(qpg_probe_lds_dma(4, A16, 1024, nullptr, static_cast<uint32_t*>(A16), nullptr) == -1);
     if (nodevice) {

@@ -240,7 +240,7 @@ def test_calib_library_exports_and_rejects():
     st = lib.qpg_calib_step
     st.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     st.restype = ctypes.c_int
-    assert st(7, 3, 100, A16, None) == EINVAL           # mode
+    assert st(8, 3, 100, A16, None) == EINVAL           # mode
     assert st(-1, 3, 100, A16, None) == EINVAL
     assert st(2, 1, 100, A16, None) == EINVAL           # waves per SIMD
     assert st(2, 5, 100, A16, None) == EINVAL

@@ -138,7 +138,7 @@ def test_step_probe_runs():
         nb = lib.qpg_calib_step_blocks(w)
         assert nb == torch.cuda.get_device_properties(0).multi_processor_count * w
         out = torch.zeros(nb * 4, dtype=torch.int64, device=DEV)
-        for mode in range(7):
+        for mode in range(8):
             assert lib.qpg_calib_step(mode, w, 20, ctypes.c_void_p(out.data_ptr()), None) == 0
             torch.cuda.synchronize()
             v = out.view(nb, 4).cpu().numpy()
