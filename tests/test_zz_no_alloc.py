@@ -2,7 +2,7 @@
 per-device scratch) against mmq_q4K (the same computation with a caller workspace): bit for
 bit, on two calls in a row, the second with a smaller input, so that stale scratch contents
 from the first call cannot leak into the second; plus the refusal of shapes beyond the
-scratch, before anything is enqueued."""
+scratch, before anything is enqueued; and the entry point inside a captured HIP graph."""
 import numpy as np
 import pytest
 
@@ -27,6 +27,37 @@ def test_noalloc_matches_workspace_entry_twice():
         assert B.mmq_q4K_noalloc(w, x, N, y) is y
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), f"{M}x{N}x{K}"
+
+
+def test_noalloc_inside_a_captured_graph():
+    """The use the entry point exists for: captured into a HIP graph (no allocation during
+    capture), replayed three times with new activations copied in between, with eager work and
+    synchronisation between the replays; every replay equals the eager mmq_q4K result."""
+    M, N, K = 64, 1024, 2048
+    W, _ = inputs.small_case("q4_K", M, N, K, seed=64)
+    w = torch.from_numpy(W.reshape(-1)).to(DEV)
+    x = torch.empty((M, K), dtype=torch.float32, device=DEV)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    x.copy_(torch.from_numpy(inputs.small_case("q4_K", M, N, K, seed=65)[1]))
+    s = torch.cuda.Stream(device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                      # warm-up call outside the capture
+        B.mmq_q4K_noalloc(w, x, N, y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.mmq_q4K_noalloc(w, x, N, y)
+    for rep in range(3):
+        X = inputs.small_case("q4_K", M, N, K, seed=66 + rep, gain=True)[1]
+        x.copy_(torch.from_numpy(X))
+        y.fill_(float("nan"))                       # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_ref = B.mmq_q4K(w, x, N)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
 
 
 def test_noalloc_largest_shape_and_refusal():
