@@ -92,3 +92,44 @@ def test_production_kernels_do_not_spill(asm_texts):
                 assert priv == 0, f"{sym}: {priv} bytes of scratch per lane"
                 assert vg <= 168, f"{sym}: {vg} VGPRs (three waves per SIMD need <= 168)"
     assert seen >= 6
+
+
+def _occupancy(lds: int, vgpr: int, waves_per_wg: int):
+    """Workgroups per CU and waves per SIMD of one instantiation on gfx950: 160 KiB of LDS per
+    CU, 512 VGPRs per SIMD lane (allocated in granules of 8), at most 8 waves per SIMD, four
+    SIMDs per CU, a workgroup's waves spread over the four."""
+    per_simd = min(8, 512 // (-(-vgpr // 8) * 8))
+    by_lds = 163840 // lds if lds else 1 << 30
+    by_waves = (per_simd * 4) // waves_per_wg
+    wgs = min(by_lds, by_waves)
+    return wgs, wgs * waves_per_wg // 4
+
+
+# production instantiations -> (waves per workgroup, workgroups per CU, waves per SIMD) the
+# designs rest on
+OCCUPANCY = [
+    ("mmq_q4k.hip", r"mmq_q4K_kernelILb0ELi1ELi2E", 4, 3, 3),     # 64-token tiles
+    ("mmq_q4k.hip", r"mmq_q4K_kernelILb0ELi1ELi1E", 4, 4, 4),     # 32-token tiles
+    ("mmq_q4k.hip", r"mmq_q4K_kernelILb0ELi3ELi2E", 12, 1, 3),    # three groups per workgroup
+    ("mmq_q4k.hip", r"mmq_q4K_kernelILb0ELi3ELi1E", 12, 1, 3),
+    ("mmq_q6k.hip", r"mmq_q6K_kernelILb0ELi1ELb0E", 4, 3, 3),     # raw blocks
+    ("mmq_q6k.hip", r"mmq_q6K_kernelILb0ELi1ELb1E", 4, 3, 3),     # prepared
+    ("mmq_q6k.hip", r"mmq_q6K_kernelILb0ELi3ELb0E", 12, 1, 3),
+    ("mmq_q6k.hip", r"mmq_q6K_kernelILb0ELi3ELb1E", 12, 1, 3),
+    ("mmq_q6k_exp.hip", r"mmq_q6K_exp_kernelILb0ELi1ELi2E", 8, 2, 4),   # eight waves per tile
+    ("mmq_q6k_exp.hip", r"mmq_q6K_exp_kernelILb0ELi3ELi1E", 12, 1, 3),
+]
+
+
+@pytest.mark.parametrize("src,pat,waves,wgs,per_simd", OCCUPANCY)
+def test_production_occupancy(asm_texts, src, pat, waves, wgs, per_simd):
+    """The LDS and VGPR budgets of each production kernel give the occupancy its design
+    assumes (a change that silently costs a workgroup per CU fails here)."""
+    text = asm_texts[src]
+    hits = [m for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S)
+            if re.search(pat, m.group(1))]
+    assert len(hits) == 1, pat
+    body = hits[0].group(2)
+    lds = int(re.search(r"\.amdhsa_group_segment_fixed_size (\d+)", body).group(1))
+    vgpr = int(re.search(r"\.amdhsa_next_free_vgpr (\d+)", body).group(1))
+    assert _occupancy(lds, vgpr, waves) == (wgs, per_simd), (pat, lds, vgpr)
