@@ -405,6 +405,14 @@ def run_shards(steps: int, warmup: int, shapes=None):
     from quantized_prefill_gemm_amd import inputs
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    # rate of torch's spin kernel (its cycle count is the shader clock's), measured once
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1_000_000)
+    e0.record(stream)
+    torch.cuda._sleep(4_000_000)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    spin_cycles_per_us = 4_000_000 / (e0.elapsed_time(e1) * 1e3)
     for form, M, N, K, what in (shapes or SHARD_SHAPES):
         wtype = "q4_K" if form == "q4K" else "q6_K"
         W, X = inputs.small_case(wtype, M, N, K, seed=1)
@@ -423,29 +431,45 @@ def run_shards(steps: int, warmup: int, shapes=None):
               "q6K_exp": B.mmq_q6K_exp_q8_sk}[form]
         fns = {"plain": lambda: plain(w, xq, M, N, K, y, stream=stream),
                "split": lambda: sk(w, xq, M, N, K, y, ws if nws else None, stream=stream)}
-        for fn in fns.values():
+        host_us = {}
+        for name, fn in fns.items():
+            h0 = time.perf_counter()
             for _ in range(warmup):
                 fn()
-        torch.cuda.synchronize()
-        # five rounds, the two entry points alternating (the clock ramps after a change of
-        # shape, so a single plain-then-split pass favours the second); median per entry
+            host_us[name] = (time.perf_counter() - h0) / warmup * 1e6
+            torch.cuda.synchronize()
+        # Each timed round starts behind a spin kernel long enough for the host to enqueue all
+        # `steps` calls (1.5x the host time the warm-up measured), so the events time the
+        # calls running back to back on the GPU, not the binding's per-call host work (which
+        # exceeds the GPU time of the smallest shapes). `host_bound` reports any round whose
+        # enqueueing outlasted its spin kernel. Five rounds, the two entry points alternating
+        # (the clock ramps after a change of shape); median per entry.
         t = {name: [] for name in fns}
+        host_bound = False
         for _ in range(5):
             for name, fn in fns.items():
+                spin_us = 1.5 * host_us[name] * steps + 200.0
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(int(spin_us * spin_cycles_per_us))
+                h0 = time.perf_counter()
                 e0.record(stream)
                 for _ in range(steps):
                     fn()
                 e1.record(stream)
+                host_bound |= e0.query()          # the GPU reached e0 before the host finished
+                enq_us = (time.perf_counter() - h0) * 1e6
                 torch.cuda.synchronize()
                 t[name].append(e0.elapsed_time(e1) / steps * 1e3)
+                host_us[name] = max(host_us[name], enq_us / steps)
         t = {name: sorted(v)[2] for name, v in t.items()}
         macs = M * N * K
         print(json.dumps({"shard": what, "form": form, "M": M, "N": N, "K": K,
                           "pieces": nws // (4 * M * N) if nws else 1,
                           "plain_us": round(t["plain"], 2), "split_us": round(t["split"], 2),
                           "plain_tmacs": round(macs / t["plain"] / 1e6, 1),
-                          "split_tmacs": round(macs / t["split"] / 1e6, 1)}), flush=True)
+                          "split_tmacs": round(macs / t["split"] / 1e6, 1),
+                          "host_us_per_call": {k: round(v, 1) for k, v in host_us.items()},
+                          "host_bound": bool(host_bound)}), flush=True)
 
 
 def copy_calibration(nbytes: int, launches: int):

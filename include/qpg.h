@@ -203,10 +203,12 @@ int mmq_q6K_exp_csums(const void* we, const void* xq, int32_t* s, int64_t M, int
  * caller's workspace ws (f32 [P][M][N]); a second kernel then sums the planes in piece
  * order into y, so the result is deterministic and independent of scheduling.
  * qpg_mmq_sk_bytes(M, N, K, form) gives the workspace size in bytes (form 0 q4_K, 1 q6_K,
- * 2 prepared q6_K, 3 expanded q6_K): P*M*N*4, or 0 when the shape needs no split
- * (more than 128 tiles of 64 x 128, 64 x 64 for form 3, or fewer than 6 super-blocks)
- * or is unsupported; with 0, ws may be null and the call is the plain entry point. P is
- * at most 8, at most 256 / tiles and keeps >= 3 super-blocks per piece. ws must be 16-byte
+ * 2 prepared q6_K, 3 expanded q6_K): P*M*N*4, or 0 when the shape needs no split (more
+ * than 128 output tiles, or too few super-blocks for two pieces) or is unsupported; with 0,
+ * ws may be null and the call is the plain entry point. Tiles are 64 tokens x 128 rows
+ * (64 x 64 for form 3; q4_K uses 32-token tiles where its 64 x 128 grid has <= 128 tiles).
+ * P is at most 8; when all M tokens fit one tile height, P <= 512 / tiles with >= 1
+ * super-block per piece, otherwise P <= 256 / tiles with >= 3 per piece. ws must be 16-byte
  * aligned and at least that large (QPG_EINVAL otherwise); it is caller-owned scratch whose
  * contents are overwritten. Calls that share ws must not overlap in time.
  */

@@ -63,7 +63,7 @@ int main(int argc, char** argv)
         CHECK(mmq_q4K_q8(A16, A16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);
         CHECK(mmq_q6K_q8(A2, A16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);   // 2-byte q6_K blocks
         CHECK(mmq_q4K_noalloc(A16, F16, F16, 64, 256, 256, nullptr) == QPG_EDEVICE);
-        CHECK(mmq_q6K_exp_q8_sk(A16, A16, F16, 64, 256, 4096, A16, 5u * 64u * 256u * 4u, nullptr) == QPG_EDEVICE);
+        CHECK(mmq_q6K_exp_q8_sk(A16, A16, F16, 64, 256, 4096, A16, 8u * 64u * 256u * 4u, nullptr) == QPG_EDEVICE);
         CHECK(qpg_calib_step_blocks(3) == 0);
     }
     std::printf("abi driver: ok\n");

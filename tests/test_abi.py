@@ -164,11 +164,17 @@ def test_q6K_expand_sizes_and_rejects(L):
 
 
 def test_splitk_workspace_sizes(L):
-    # P = min(8, 256 // tiles, (K/256) // 3) when tiles <= 128, else no split (0 bytes); q4_K
-    # tiles are 32 x 128 when the 64 x 128 grid has <= 128 tiles (or M <= 256 and > 256 tiles)
+    # P = min(8, 256 // tiles, (K/256) // 3) when tiles <= 128, else no split (0 bytes); when M
+    # fits one tile height, P = min(8, 512 // tiles, K/256) instead. q4_K tiles are 32 x 128
+    # when the 64 x 128 grid has <= 128 tiles (or M <= 256 and > 256 tiles)
     assert L.qpg_mmq_sk_bytes(512, 512, 4096, 0) == 4 * 512 * 512 * 4      # 64 tiles of 32 rows -> 4
     assert L.qpg_mmq_sk_bytes(512, 1376, 4096, 0) == 0                     # 176 tiles of 32 rows
-    assert L.qpg_mmq_sk_bytes(16, 4096, 4096, 0) == 5 * 16 * 4096 * 4      # 32 tiles of 32 rows -> 5
+    assert L.qpg_mmq_sk_bytes(16, 4096, 4096, 0) == 8 * 16 * 4096 * 4      # one row of 32 tiles -> 8
+    assert L.qpg_mmq_sk_bytes(32, 11008, 4096, 0) == 5 * 32 * 11008 * 4    # one row of 86 tiles -> 5
+    assert L.qpg_mmq_sk_bytes(33, 4096, 4096, 0) == 4 * 33 * 4096 * 4      # two rows of 32 -> 4
+    assert L.qpg_mmq_sk_bytes(64, 4096, 4096, 3) == 8 * 64 * 4096 * 4      # one row of 64 tiles (64 x 64) -> 8
+    assert L.qpg_mmq_sk_bytes(16, 128, 512, 0) == 2 * 16 * 128 * 4         # one tile, 2 SB -> 2
+    assert L.qpg_mmq_sk_bytes(16, 128, 256, 0) == 0                        # one super-block
     assert L.qpg_mmq_sk_bytes(512, 512, 4096, 1) == 5 * 512 * 512 * 4      # q6_K: 32 tiles of 64 rows -> 5
     assert L.qpg_mmq_sk_bytes(512, 512, 11008, 1) == 8 * 512 * 512 * 4     # 32 tiles, 43 SB -> 8
     assert L.qpg_mmq_sk_bytes(512, 512, 11008, 2) == 8 * 512 * 512 * 4
@@ -220,7 +226,7 @@ def test_valid_call_without_device_reports_edevice(L):
     assert L.mmq_q6K_exp_q8(A16, A16, A16, 64, 256, 256, None) == EDEVICE
     # no split for this shape: the workspace may be absent
     assert L.mmq_q4K_q8_sk(A16, A16, A16, 64, 256, 1280, None, 0, None) == EDEVICE
-    assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 64, 256, 4096, A16, 5 * 64 * 256 * 4, None) == EDEVICE
+    assert L.mmq_q6K_exp_q8_sk(A16, A16, A16, 64, 256, 4096, A16, 8 * 64 * 256 * 4, None) == EDEVICE
 
 
 CALIB = os.path.join(ROOT, "quantized_prefill_gemm_amd", "libqpg_calib.so")

@@ -393,10 +393,11 @@ def test_splitk_matches_oracle(form, M, N, K):
 
 @pytest.mark.parametrize("form", SK_FORMS)
 def test_splitk_without_split_is_the_plain_entry(form):
-    """Shapes that need no split (many tiles, or < 6 super-blocks) take no workspace and
-    give the plain entry point's output bit for bit."""
+    """Shapes that need no split (many tiles, too few super-blocks for two pieces of three
+    with several token-tile rows, or one super-block) take no workspace and give the plain
+    entry point's output bit for bit."""
     wtype = "q4_K" if form == "q4K" else "q6_K"
-    for M, N, K in ((64, 100, 1280), (640, 2100, 1024)):
+    for M, N, K in ((100, 100, 1280), (640, 2100, 1024), (16, 100, 256)):
         assert B.mmq_sk_bytes(M, N, K, form) == 0
         say(f"[split-K no split {form} {M}x{N}x{K}]")
         W, X = inputs.small_case(wtype, M, N, K, seed=10)

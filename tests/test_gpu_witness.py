@@ -265,7 +265,8 @@ EXACT_CASES = [
     ("q4_K 512x1376x4096", "q4K", 512, 1376, 4096, "split3/tm32", None),
     ("q4_K 128x4096x4096", "q4K", 128, 4096, 4096, "split3/tm32", None),
     ("q4_K 256x11008x4096", "q4K", 256, 11008, 4096, "one-group/tm32", None),
-    ("q4_K K-split 16x4096x4096", "q4K", 16, 4096, 4096, "split3/tm32", 5),
+    ("q4_K K-split 16x4096x4096", "q4K", 16, 4096, 4096, "one-group/tm32", 8),
+    ("q4_K K-split 64x4096x4096", "q4K", 64, 4096, 4096, "split3/tm32", 4),
     ("q6_K raw 512x4096x11008", "raw", 512, 4096, 11008, "split3", None),
     ("q6_K raw 1024x4096x11008", "raw", 1024, 4096, 11008, "one-group", None),
     ("q6_K prepared 512x4096x11008", "prep", 512, 4096, 11008, "split3", None),
