@@ -82,6 +82,5 @@ hipError_t qpg_launch_mmq_q6K_prep(const void* wp, const void* xq, float* y, int
 hipError_t qpg_launch_q6K_expand(const void* w, void* we, int64_t N, int64_t K, hipStream_t s);
 hipError_t qpg_launch_mmq_q6K_exp(const void* we, const void* xq, float* y, int32_t* csums,
                                   int64_t M, int64_t N, int64_t K, int pieces, hipStream_t s);
-// y[i] = sum over p < pieces of ws[p * MN + i], in piece order (deterministic); pieces in 2..8
-// (hipErrorInvalidValue otherwise).
+// y[i] = sum over p < pieces of ws[p * MN + i], in piece order (deterministic).
 hipError_t qpg_launch_splitk_reduce(const float* ws, float* y, int64_t MN, int pieces, hipStream_t s);

@@ -58,6 +58,7 @@ hipError_t launch_reduce(const float* ws, float* y, int64_t MN, hipStream_t s)
 
 }  // namespace qpg
 
+// pieces in 2..8 (the K-split entry points' range); hipErrorInvalidValue otherwise
 hipError_t qpg_launch_splitk_reduce(const float* ws, float* y, int64_t MN, int pieces, hipStream_t s)
 {
     switch (pieces) {
