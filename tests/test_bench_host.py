@@ -40,6 +40,15 @@ def test_traffic_guarded_by_kernel_hash(tmp_path, monkeypatch):
     assert bench.load_traffic() is None
 
 
+def test_committed_counters_describe_the_committed_kernel():
+    """The HBM counters in profiles/ were taken on exactly the q4_K kernel source in the tree
+    (mmq_q4k.hip and qpg_common.h), so the bench line carries its traffic figure; any edit of
+    those files, comments included, needs the FETCH_SIZE / WRITE_SIZE runs taken again."""
+    t = json.load(open(bench.TRAFFIC_FILE))
+    assert t["kernel_hash"] == bench.kernel_hash()
+    assert bench.load_traffic() == t["hbm_bytes_per_launch"]
+
+
 def test_traffic_figure_from_counters():
     t = json.load(open(bench.TRAFFIC_FILE))
     cal = t["copy_calibration"]
