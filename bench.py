@@ -234,11 +234,11 @@ STEP_MODES = {0: "mfma_only", 1: "fold_only", 2: "kernel_step", 3: "mfma_and_ind
               6: "kernel_step_operands_from_lds_one_step_ahead", 7: "kernel_step_fold_in_groups_of_4"}
 
 
-def measured_step_ceiling(waves=(2, 3, 4), iters: int = 4000):
+def measured_step_ceiling(waves=(1, 2, 3, 4), iters: int = 4000):
     """The q4_K kernel's compute step alone (libqpg_calib.so qpg_calib_step: one
     v_mfma_i32_32x32x32_i8 issued a step ahead plus the 32 fold FMAs of the previous result,
-    per wave and step; no memory traffic, barriers, decode or min term), at 2-4 waves per
-    SIMD. Each mode is timed with HIP events around one launch; the rate is counted in the
+    per wave and step; no memory traffic, barriers, decode or min term), at 1-4 waves per
+    SIMD (one: a short prompt's split, one four-wave workgroup per CU). Each mode is timed with HIP events around one launch; the rate is counted in the
     int8 ops of the MFMAs (2 per MAC) the steps stand for, also for the fold-only mode.
     Returns the rate of the kernel's step at its production occupancy (3 waves per SIMD) as
     the ceiling of its arithmetic, plus every mode and occupancy."""

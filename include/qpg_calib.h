@@ -38,8 +38,9 @@ int qpg_calib_mfma_i8(int64_t blocks, int64_t iters, uint64_t* out, void* stream
  *   operands (B, raw weights, d*sc, da pair) read from LDS as the kernel reads them;
  *   6: mode 5 with every LDS operand read one step ahead (double-buffered in registers);
  *   7: the kernel's step with its fold issued in groups of four independent FMAs.
- * waves_per_simd in {2, 3, 4}: the launch holds exactly that many waves on every SIMD
- * (qpg_calib_step_blocks(w) workgroups of four waves, LDS sized so that w fit a CU).
+ * waves_per_simd in {1, 2, 3, 4}: the launch holds exactly that many waves on every SIMD
+ * (qpg_calib_step_blocks(w) workgroups of four waves, LDS sized so that w fit a CU; one
+ * wave per SIMD is the situation of a short prompt's split, one workgroup per CU).
  * Every wave runs iters x 8 steps. out: device pointer to qpg_calib_step_blocks(w) * 4
  * uint64 values, 8-byte aligned, owned by the caller, written as for qpg_calib_mfma_i8.
  * Asynchronous on `stream`. Returns 0, -1 (bad mode, w, iters or null out), -2 (alignment),
@@ -47,7 +48,7 @@ int qpg_calib_mfma_i8(int64_t blocks, int64_t iters, uint64_t* out, void* stream
 int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream);
 
 /* Workgroups qpg_calib_step launches for waves_per_simd (CUs x w), 0 if w is outside
- * {2, 3, 4} or the current device is not gfx950. */
+ * {1, 2, 3, 4} or the current device is not gfx950. */
 int64_t qpg_calib_step_blocks(int waves_per_simd);
 
 /* Matrix-instruction layout probe: one wave executes one instruction, lane l's source

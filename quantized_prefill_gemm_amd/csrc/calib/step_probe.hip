@@ -209,6 +209,7 @@ template <int MODE>
 hipError_t launch_mode(int w, unsigned blocks, int iters, uint64_t* out, hipStream_t s)
 {
     switch (w) {
+    case 1: hipLaunchKernelGGL((step_kernel<MODE, 1>), dim3(blocks), dim3(256), 0, s, iters, out); break;
     case 2: hipLaunchKernelGGL((step_kernel<MODE, 2>), dim3(blocks), dim3(256), 0, s, iters, out); break;
     case 3: hipLaunchKernelGGL((step_kernel<MODE, 3>), dim3(blocks), dim3(256), 0, s, iters, out); break;
     default: hipLaunchKernelGGL((step_kernel<MODE, 4>), dim3(blocks), dim3(256), 0, s, iters, out); break;
@@ -221,13 +222,13 @@ hipError_t launch_mode(int w, unsigned blocks, int iters, uint64_t* out, hipStre
 extern "C" int64_t qpg_calib_step_blocks(int waves_per_simd)
 {
     int cus = 0;
-    if (waves_per_simd < 2 || waves_per_simd > 4 || check_device(&cus) != 0) return 0;
+    if (waves_per_simd < 1 || waves_per_simd > 4 || check_device(&cus) != 0) return 0;
     return (int64_t)cus * waves_per_simd;
 }
 
 extern "C" int qpg_calib_step(int mode, int waves_per_simd, int64_t iters, uint64_t* out, void* stream)
 {
-    if (!out || mode < 0 || mode > 7 || waves_per_simd < 2 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
+    if (!out || mode < 0 || mode > 7 || waves_per_simd < 1 || waves_per_simd > 4 || iters < 1 || iters > 10000000)
         return -1;
     if (((uintptr_t)out & 7) != 0) return -2;
     int cus = 0;

@@ -248,7 +248,7 @@ def test_calib_library_exports_and_rejects():
     st.restype = ctypes.c_int
     assert st(8, 3, 100, A16, None) == EINVAL           # mode
     assert st(-1, 3, 100, A16, None) == EINVAL
-    assert st(2, 1, 100, A16, None) == EINVAL           # waves per SIMD
+    assert st(2, 0, 100, A16, None) == EINVAL           # waves per SIMD
     assert st(2, 5, 100, A16, None) == EINVAL
     assert st(2, 3, 0, A16, None) == EINVAL             # iters
     assert st(2, 3, 100, None, None) == EINVAL

@@ -127,14 +127,14 @@ def test_magic_accumulator_exact_at_extremes(probe, kind, K, wmax, wmin):
 
 
 def test_step_probe_runs():
-    """The compute-step probe (all modes, 2-4 waves per SIMD) reports a tick count for every
+    """The compute-step probe (all modes, 1-4 waves per SIMD) reports a tick count for every
     workgroup."""
     lib = ctypes.CDLL(CALIB)
     lib.qpg_calib_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.qpg_calib_step.restype = ctypes.c_int
     lib.qpg_calib_step_blocks.argtypes = [ctypes.c_int]
     lib.qpg_calib_step_blocks.restype = ctypes.c_int64
-    for w in (2, 3, 4):
+    for w in (1, 2, 3, 4):
         nb = lib.qpg_calib_step_blocks(w)
         assert nb == torch.cuda.get_device_properties(0).multi_processor_count * w
         out = torch.zeros(nb * 4, dtype=torch.int64, device=DEV)
